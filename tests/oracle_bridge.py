@@ -1,0 +1,65 @@
+"""Test glue: hand the generator's tensors to the CPU oracle.
+
+Converts torch storage (fp32, bf16 bit patterns, fp8 codes + block scales) into
+the oracle's float64 inputs through the oracle's own decoders, and maps a
+LayerShape onto the oracle's Spec.  Nothing here computes the layer.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from routed_expert_moe_amd.configs import LayerShape
+
+
+def spec_of(shape: LayerShape) -> oracle.Spec:
+    return oracle.Spec(n_routed=shape.n_routed, n_groups=shape.n_groups,
+                       topk_groups=shape.topk_groups, top_k=shape.top_k, score=shape.score,
+                       route_scale=shape.route_scale, norm_topk=shape.norm_topk,
+                       add_residual=shape.add_residual)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy().astype(np.float64)
+    if t.dtype == torch.bfloat16:
+        return oracle.decode_bf16(t.view(torch.int16).numpy().view(np.uint16))
+    raise TypeError(t.dtype)
+
+
+def weight_f64(q: torch.Tensor, scale, kind: str) -> np.ndarray:
+    if kind == "fp8":
+        return oracle.dequant_e4m3_block128(q.detach().cpu().numpy(), scale.detach().cpu().numpy())
+    return to_f64(q)
+
+
+def expert_fn(layer):
+    kind = layer.shape.weight
+
+    def get(e: int):
+        s13 = layer.w13_scale[e] if kind == "fp8" else None
+        s2 = layer.w2_scale[e] if kind == "fp8" else None
+        return weight_f64(layer.w13[e], s13, kind), weight_f64(layer.w2[e], s2, kind)
+    return get
+
+
+def shared_pair(layer):
+    if layer.sw13 is None:
+        return None
+    kind = layer.shape.weight
+    return (weight_f64(layer.sw13, layer.sw13_scale, kind),
+            weight_f64(layer.sw2, layer.sw2_scale, kind))
+
+
+def bias_f64(layer):
+    return None if layer.bias is None else layer.bias.detach().cpu().numpy().astype(np.float64)
+
+
+def run_oracle(layer, tokens=None, force_idx=None, x=None):
+    """Oracle forward of `layer` (optionally on another x and a token subset)."""
+    xx = to_f64(layer.x if x is None else x)
+    return oracle.moe_layer(xx, to_f64(layer.w_gate), bias_f64(layer), expert_fn(layer),
+                            shared_pair(layer), spec_of(layer.shape), tokens=tokens,
+                            force_idx=force_idx)
