@@ -1,0 +1,199 @@
+/*
+ * moe355.h - C ABI of an MI355X (gfx950) forward pass for one DeepSeekMoE layer.
+ *
+ * The layer (DeepSeek-V3 notes page, 73biji.xyz/llm_pp_dsv3, "DeepSeekMoE"
+ * paragraph, total-output equation):
+ *
+ *     h'_t = u_t + FFN_share(u_t) + sum_{r in S_t} g_{r,t} FFN_r(u_t)
+ *
+ * with S_t and g chosen by the gate (same page, gate flow in five steps):
+ * sigmoid scores (plus a per-expert bias that only steers selection), a
+ * group-limited top-k, and the unbiased scores at the chosen experts,
+ * renormalised and scaled by route_scale.  The conventional softmax top-k
+ * gate of the same paragraph is the other scoring mode.  Every expert FFN is
+ * a SwiGLU, W2 (silu(W1 u) * (W3 u)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless a comment says "host".  All buffers
+ *    are row-major and dense; "K-contiguous" means the last dimension is the
+ *    reduction dimension.
+ *  - The caller owns every buffer.  Inputs are read only; outputs are fully
+ *    overwritten.  The library allocates no device memory and keeps no mutable
+ *    global state, so calls on different streams are independent.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work: results are ready when the stream is
+ *    synchronised.  Nothing is read back to the host.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    any error status no kernel has been launched.  T == 0 returns MOE_OK and
+ *    launches nothing.  A launch failure returns MOE_ERR_DEVICE; a fault inside
+ *    a kernel surfaces at the caller's next synchronisation, as with any HIP call.
+ *  - moe_last_error() returns a thread-local message for the last failing call.
+ *  - Same inputs give bitwise-identical outputs (no atomics on any value path;
+ *    every reduction has a fixed order).
+ */
+#ifndef MOE355_H
+#define MOE355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* bad configuration, size or NULL pointer */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid layer, but outside this library's kernels */
+  MOE_ERR_WORKSPACE = 3,     /* workspace / routing buffer too small */
+  MOE_ERR_DEVICE = 4         /* a HIP call or kernel launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,               /* IEEE binary32 */
+  MOE_BF16 = 1,              /* bfloat16 */
+  MOE_FP8_E4M3_B128 = 2      /* OCP e4m3fn codes, one fp32 scale per 128x128 block */
+} moe_dtype;
+
+typedef enum {
+  MOE_SCORE_SIGMOID = 0,     /* s = sigmoid(W_g u); ranked key s + b */
+  MOE_SCORE_SOFTMAX = 1      /* p = softmax(W_g u) over all experts; ranked key = logit (p + b with a bias) */
+} moe_score;
+
+/* The layer's hyper-parameters, named as in the DeepSeek-V3 model.py config
+ * table on the notes page (dim, n_routed_experts, n_shared_experts, n_expert_groups,
+ * n_limited_groups -> topk_groups, n_activated_experts -> top_k, route_scale,
+ * moe_inter_dim -> inter_dim, score_func). */
+typedef struct moe_config {
+  int32_t dim;           /* model width D */
+  int32_t n_routed;      /* routed experts E, 1..512 */
+  int32_t n_shared;      /* shared experts S >= 0; they act as one SwiGLU of hidden S*inter_dim */
+  int32_t n_groups;      /* routing groups G (E % G == 0); 1 = no group limit */
+  int32_t topk_groups;   /* groups kept per token, 1..G */
+  int32_t top_k;         /* experts per token K, 1..min(32, topk_groups*E/G) */
+  int32_t inter_dim;     /* hidden size I of one expert */
+  float route_scale;     /* finite, > 0 */
+  int32_t score_func;    /* moe_score */
+  int32_t norm_topk;     /* -1: sigmoid renormalises the chosen weights, softmax does not; 0/1 force */
+  int32_t act_dtype;     /* x, out, w_gate, intermediates: MOE_F32 or MOE_BF16 */
+  int32_t weight_dtype;  /* routed + shared expert weights: MOE_F32 (with act F32), MOE_BF16 or
+                            MOE_FP8_E4M3_B128 (with act BF16) */
+  int32_t add_residual;  /* 1: out includes u_t (the total-output equation); 0: out = FFN terms only */
+} moe_config;
+
+/* Expert weights.  fp8 scale tensors are fp32 with one entry per 128x128 block
+ * of the matrix they scale (NULL for other dtypes). */
+typedef struct moe_weights {
+  const void *w_gate;        /* [E, D] act dtype, K-contiguous (one row per routed expert) */
+  const float *bias;         /* [E] fp32, or NULL (no bias: group score = max key) */
+  const void *w13;           /* [E, 2I, D]: rows [0,I) = W1 (gate proj), [I,2I) = W3 (up proj) */
+  const float *w13_scale;    /* fp8: [E, 2I/128, D/128] */
+  const void *w2;            /* [E, D, I]  (down proj, K-contiguous) */
+  const float *w2_scale;     /* fp8: [E, D/128, I/128] */
+  const void *sw13;          /* [2SI, D]: rows [0,SI) gate, [SI,2SI) up; NULL iff S == 0 */
+  const float *sw13_scale;   /* fp8: [2SI/128, D/128] */
+  const void *sw2;           /* [D, SI] */
+  const float *sw2_scale;    /* fp8: [D/128, SI/128] */
+} moe_weights;
+
+/* Dispatch state written by moe_permute: the T*K (token, slot) pairs sorted by
+ * expert into row ranges padded to a multiple of tile_m.  Pair id p = t*K + k.
+ * Build it with moe_routing_init over one caller buffer of moe_routing_size bytes. */
+typedef struct moe_routing {
+  int32_t tile_m;        /* host: rows per expert tile (chosen by the library for (cfg, T)) */
+  int32_t max_rows;      /* host: capacity in rows = T*K + E*(tile_m-1) (rounded up) */
+  int32_t max_tiles;     /* host: capacity of the tile lists = ceil(T*K/tile_m) + E */
+  int32_t pad_;
+  int32_t *counts;       /* [E]          pairs routed to each expert */
+  int32_t *expert_off;   /* [E+1]        first row of each expert (multiples of tile_m);
+                                         expert_off[E] = rows in use */
+  int32_t *sorted_pair;  /* [max_rows]   pair id held by each row, -1 in padding rows;
+                                         within an expert pairs ascend by id (stable) */
+  int32_t *pair_row;     /* [T*K]        row of each pair (inverse of sorted_pair) */
+  int32_t *tile_expert;  /* [max_tiles]  expert of each tile, tiles in row order */
+  int32_t *tile_row;     /* [max_tiles]  first row of each tile */
+  int32_t *n_tiles;      /* [1]          tiles in use */
+  int32_t *scratch;      /* internal */
+} moe_routing;
+
+/* ---- host-only queries (no device access) -------------------------------- */
+
+/* Checks a configuration: E % G == 0, 1 <= topk_groups <= G,
+ * 1 <= top_k <= topk_groups*E/G, group size >= 2 when a bias makes the group
+ * score a top-2 sum (checked at call time), route_scale finite and > 0,
+ * dims > 0.  Returns MOE_ERR_UNSUPPORTED for valid layers outside the
+ * kernels' limits: E > 512, top_k > 32, G > 32, dtype pairs other than
+ * (F32,F32), (BF16,BF16), (BF16,FP8); D or I not a multiple of 8 (of 128 for fp8). */
+moe_status moe_validate(const moe_config *cfg);
+
+/* Bytes of one routing buffer for T tokens (host out-param *bytes). */
+moe_status moe_routing_size(const moe_config *cfg, int64_t T, size_t *bytes);
+
+/* Carves a routing buffer (device memory of >= moe_routing_size bytes, 256-byte
+ * aligned) into the arrays of *r (host struct).  Host only: nothing is written
+ * to the device. */
+moe_status moe_routing_init(const moe_config *cfg, int64_t T, void *buf, size_t bytes,
+                            moe_routing *r);
+
+/* Bytes of the workspace moe_forward needs for T tokens (host out-param). */
+moe_status moe_workspace_size(const moe_config *cfg, int64_t T, size_t *bytes);
+
+const char *moe_status_str(moe_status s);
+const char *moe_last_error(void);   /* thread-local; "" after a successful call */
+
+/* ---- the forward pass, step by step ---------------------------------------- */
+
+/* Gate (notes page, gate flow steps 1-5).
+ *   x        [T, D] act dtype;  w_gate [E, D] act dtype;  bias [E] fp32 or NULL
+ *   logits   [T, E] fp32 out:   x W_g^T with fp32 accumulation
+ *   topk_idx [T, K] int32 out:  chosen experts, ascending; ties rank the lower
+ *                               expert (and group) index first
+ *   topk_w   [T, K] fp32 out:   unbiased score at each chosen expert, renormalised
+ *                               (per norm_topk) and times route_scale
+ *   keys     [T, E] fp32 out or NULL: the ranked key of every expert before
+ *                               group masking (sigmoid: s+b; softmax: logit, or p+b) */
+moe_status moe_gate(const moe_config *cfg, int64_t T, const void *x, const void *w_gate,
+                    const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
+                    float *keys, void *stream);
+
+/* Dispatch (replaces the per-expert gather of the notes page's MoE forward,
+ * step 2): histogram of experts over the T*K pairs, exclusive scan of the
+ * padded counts, stable scatter into expert-sorted rows, tile lists.
+ *   topk_idx [T, K] int32 (each entry in [0, E));  r from moe_routing_init. */
+moe_status moe_permute(const moe_config *cfg, int64_t T, const int32_t *topk_idx,
+                       const moe_routing *r, void *stream);
+
+/* Expert FFNs: for every used row i of expert e holding pair p = t*K + k,
+ *   h[i]       = silu(W1_e x_t) * (W3_e x_t)               [max_rows, I] act dtype
+ *   y_pairs[i] = W2_e h[i]                                   [max_rows, D] act dtype
+ * and, when z != NULL, the shared expert on every token:
+ *   hs[t] = silu(SW1 x_t) * (SW3 x_t)  [T, S*I];  z[t] = SW2 hs[t]  [T, D]  act dtype
+ * Accumulation is fp32; h, hs, y_pairs and z are rounded once to the act dtype.
+ * Padding rows of h and y_pairs hold unspecified values.  r must hold the
+ * output of moe_permute for the same T and topk_idx. */
+moe_status moe_expert_ffn(const moe_config *cfg, int64_t T, const void *x,
+                          const moe_routing *r, const moe_weights *w, void *h, void *y_pairs,
+                          void *hs, void *z, void *stream);
+
+/* Combine (total-output equation): for every token t
+ *   out[t] = (add_residual ? u[t] : 0) + (z ? z[t] : 0)
+ *            + sum over k in ascending expert order of topk_w[t,k] * y_pairs[pair_row[t*K+k]]
+ * summed in fp32 in exactly that order, rounded once to the act dtype.
+ *   u [T, D], z [T, D] or NULL, out [T, D]: act dtype;  topk_w [T, K] fp32. */
+moe_status moe_combine(const moe_config *cfg, int64_t T, const void *u, const void *z,
+                       const void *y_pairs, const moe_routing *r, const float *topk_w,
+                       void *out, void *stream);
+
+/* Whole layer: moe_gate -> moe_permute -> moe_expert_ffn -> moe_combine on one
+ * stream, every intermediate in `ws` (>= moe_workspace_size bytes, 256-byte aligned).
+ *   x [T, D] act dtype;  out [T, D] act dtype (must not alias x)
+ *   topk_idx [T, K] int32 / topk_w [T, K] fp32: optional copies of the routing (NULL = skip) */
+moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                       void *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE355_H */

@@ -1,0 +1,487 @@
+// Host side of the C ABI declared in moe355.h: validation, planning, buffer
+// carving and the launch sequence of the layer forward.  Nothing here touches
+// device memory except through the kernel launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.hpp"
+
+namespace moe {
+int64_t permute_scratch_ints(int64_t P, int E);
+}
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+moe_status device_fail(hipError_t e, const char *what) {
+  return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t act_bytes(const moe_config &c) { return c.act_dtype == MOE_F32 ? 4 : 2; }
+size_t weight_bytes(const moe_config &c) {
+  return c.weight_dtype == MOE_F32 ? 4 : c.weight_dtype == MOE_BF16 ? 2 : 1;
+}
+
+Plan plan_for(const moe_config &c, int64_t T) {
+  if (c.act_dtype == MOE_F32) return Plan{PATH_F32, kF32TileM};
+  if (c.weight_dtype == MOE_FP8_E4M3_B128) return Plan{PATH_SKINNY, kSkinnyTileM};
+  const int64_t avg_rows = T * c.top_k / c.n_routed;
+  if (avg_rows < 32) return Plan{PATH_SKINNY, kSkinnyTileM};
+  return Plan{PATH_MFMA, kMfmaTileM};
+}
+
+struct RoutingLayout {
+  int tile_m;
+  int64_t max_rows, max_tiles, P;
+  size_t off_counts, off_expert_off, off_sorted, off_pair_row, off_tile_expert, off_tile_row,
+      off_ntiles, off_scratch, total;
+};
+
+RoutingLayout routing_layout(const moe_config &c, int64_t T) {
+  RoutingLayout L{};
+  const Plan p = plan_for(c, T);
+  L.tile_m = p.tile_m;
+  L.P = T * c.top_k;
+  L.max_rows = static_cast<int64_t>(round_up(static_cast<size_t>(L.P + static_cast<int64_t>(c.n_routed) * (p.tile_m - 1)), p.tile_m));
+  L.max_tiles = L.max_rows / p.tile_m;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = round_up(o + bytes, kAlign);
+    return at;
+  };
+  L.off_counts = take(4 * static_cast<size_t>(c.n_routed));
+  L.off_expert_off = take(4 * static_cast<size_t>(c.n_routed + 1));
+  L.off_sorted = take(4 * static_cast<size_t>(L.max_rows));
+  L.off_pair_row = take(4 * static_cast<size_t>(L.P));
+  L.off_tile_expert = take(4 * static_cast<size_t>(L.max_tiles));
+  L.off_tile_row = take(4 * static_cast<size_t>(L.max_tiles));
+  L.off_ntiles = take(4);
+  L.off_scratch = take(4 * static_cast<size_t>(permute_scratch_ints(L.P, c.n_routed)));
+  L.total = o;
+  return L;
+}
+
+struct WorkspaceLayout {
+  RoutingLayout rl;
+  size_t off_logits, off_idx, off_w, off_routing, off_h, off_hs, off_y, off_z, total;
+};
+
+WorkspaceLayout workspace_layout(const moe_config &c, int64_t T) {
+  WorkspaceLayout W{};
+  W.rl = routing_layout(c, T);
+  const size_t ab = act_bytes(c);
+  const int64_t SI = static_cast<int64_t>(c.n_shared) * c.inter_dim;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = round_up(o + bytes, kAlign);
+    return at;
+  };
+  W.off_logits = take(4 * static_cast<size_t>(T) * c.n_routed);
+  W.off_idx = take(4 * static_cast<size_t>(W.rl.P));
+  W.off_w = take(4 * static_cast<size_t>(W.rl.P));
+  W.off_routing = take(W.rl.total);
+  W.off_h = take(ab * static_cast<size_t>(W.rl.max_rows) * c.inter_dim);
+  W.off_hs = take(ab * static_cast<size_t>(T) * SI);
+  W.off_y = take(ab * static_cast<size_t>(W.rl.max_rows) * c.dim);
+  W.off_z = take(ab * static_cast<size_t>(T) * c.dim);
+  W.total = o;
+  return W;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_cfg(const moe_config *c) {
+  if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->dim <= 0 || c->inter_dim <= 0) return fail(MOE_ERR_INVALID_ARG, "dim and inter_dim must be > 0");
+  if (c->n_routed <= 0) return fail(MOE_ERR_INVALID_ARG, "n_routed must be > 0");
+  if (c->n_shared < 0) return fail(MOE_ERR_INVALID_ARG, "n_shared must be >= 0");
+  if (c->n_groups <= 0 || c->n_routed % c->n_groups != 0)
+    return fail(MOE_ERR_INVALID_ARG, "n_groups must divide n_routed (got %d, %d)", c->n_groups, c->n_routed);
+  if (c->topk_groups < 1 || c->topk_groups > c->n_groups)
+    return fail(MOE_ERR_INVALID_ARG, "topk_groups must be in [1, n_groups]");
+  const int gsz = c->n_routed / c->n_groups;
+  if (c->top_k < 1 || c->top_k > c->topk_groups * gsz)
+    return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, topk_groups * n_routed / n_groups]");
+  if (!isfinite(c->route_scale) || !(c->route_scale > 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "route_scale must be finite and > 0");
+  if (c->score_func != MOE_SCORE_SIGMOID && c->score_func != MOE_SCORE_SOFTMAX)
+    return fail(MOE_ERR_INVALID_ARG, "unknown score_func %d", c->score_func);
+  if (c->norm_topk < -1 || c->norm_topk > 1) return fail(MOE_ERR_INVALID_ARG, "norm_topk must be -1, 0 or 1");
+  if (c->add_residual != 0 && c->add_residual != 1) return fail(MOE_ERR_INVALID_ARG, "add_residual must be 0 or 1");
+  const bool pair_ok = (c->act_dtype == MOE_F32 && c->weight_dtype == MOE_F32) ||
+                       (c->act_dtype == MOE_BF16 && c->weight_dtype == MOE_BF16) ||
+                       (c->act_dtype == MOE_BF16 && c->weight_dtype == MOE_FP8_E4M3_B128);
+  if (c->act_dtype < MOE_F32 || c->act_dtype > MOE_BF16 || c->weight_dtype < MOE_F32 ||
+      c->weight_dtype > MOE_FP8_E4M3_B128)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (!pair_ok) return fail(MOE_ERR_UNSUPPORTED, "unsupported (act, weight) dtype pair (%d, %d)", c->act_dtype, c->weight_dtype);
+  if (c->n_routed > 512) return fail(MOE_ERR_UNSUPPORTED, "n_routed > 512");
+  if (c->top_k > 32) return fail(MOE_ERR_UNSUPPORTED, "top_k > 32");
+  if (c->n_groups > 64) return fail(MOE_ERR_UNSUPPORTED, "n_groups > 64");
+  if (c->dim % 8 != 0 || c->inter_dim % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "dim and inter_dim must be multiples of 8");
+  if (c->weight_dtype == MOE_FP8_E4M3_B128 && (c->dim % 128 != 0 || c->inter_dim % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 block scales need dim and inter_dim multiples of 128");
+  return MOE_OK;
+}
+
+moe_status check_T(const moe_config &c, int64_t T) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+  const int64_t rows = T * c.top_k + static_cast<int64_t>(c.n_routed) * 128;
+  if (T > (1ll << 31) / 64 || rows >= (1ll << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T too large for 32-bit row indices");
+  return MOE_OK;
+}
+
+moe_status check_bias(const moe_config &c, const float *bias) {
+  if (bias != nullptr && c.n_groups > 1 && c.n_routed / c.n_groups < 2)
+    return fail(MOE_ERR_INVALID_ARG, "with a bias the group score is a top-2 sum: group size must be >= 2");
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)            \
+  do {                           \
+    const moe_status s_ = (expr); \
+    if (s_ != MOE_OK) return s_; \
+  } while (0)
+
+#define MOE_NEED(p, name)                                                       \
+  do {                                                                          \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);   \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define MOE_OPT(p, name)                                                        \
+  do {                                                                          \
+    if ((p) != nullptr && !aligned16(p))                                        \
+      return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);      \
+  } while (0)
+
+moe_status check_routing(const moe_config &c, int64_t T, const moe_routing *r) {
+  if (r == nullptr) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  const RoutingLayout L = routing_layout(c, T);
+  if (r->tile_m != L.tile_m || r->max_rows != L.max_rows || r->max_tiles != L.max_tiles)
+    return fail(MOE_ERR_INVALID_ARG, "routing was built for another configuration or T");
+  if (!r->counts || !r->expert_off || !r->sorted_pair || !r->pair_row || !r->tile_expert ||
+      !r->tile_row || !r->n_tiles || !r->scratch)
+    return fail(MOE_ERR_INVALID_ARG, "routing has NULL arrays");
+  return MOE_OK;
+}
+
+// ---- the step implementations (arguments already validated) ---------------
+moe_status do_gate(const moe_config &c, int64_t T, const void *x, const void *w_gate,
+                   const float *bias, float *logits, int32_t *idx, float *w, float *keys,
+                   hipStream_t st) {
+  Segment s{};
+  s.a = x;
+  s.lda = c.dim;
+  s.a_rows = static_cast<int32_t>(T);
+  s.b = w_gate;
+  s.n = c.n_routed;
+  s.k = c.dim;
+  s.c = logits;
+  s.ldc = c.n_routed;
+  hipError_t e;
+  if (c.act_dtype == MOE_F32) {
+    s.n_tiles_host = static_cast<int32_t>((T + kF32TileM - 1) / kF32TileM);
+    e = launch_gemm_f32(&s, 1, kF32TileM, EPI_STORE, st);
+  } else if (T >= 64) {
+    s.n_tiles_host = static_cast<int32_t>((T + kMfmaTileM - 1) / kMfmaTileM);
+    e = launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
+  } else {
+    s.n_tiles_host = static_cast<int32_t>((T + kSkinnyTileM - 1) / kSkinnyTileM);
+    e = launch_gemm_skinny(&s, 1, EPI_STORE, false, true, st);
+  }
+  if (e != hipSuccess) return device_fail(e, "gate logits launch");
+  e = launch_gate_route(c, T, logits, bias, idx, w, keys, st);
+  if (e != hipSuccess) return device_fail(e, "gate route launch");
+  return ok();
+}
+
+moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routing &r,
+                  const moe_weights &w, void *h, void *y, void *hs, void *z, hipStream_t st) {
+  const Plan p = plan_for(c, T);
+  const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim;
+  const bool fp8 = c.weight_dtype == MOE_FP8_E4M3_B128;
+  const bool shared = z != nullptr && c.n_shared > 0;
+  const int32_t dense_tiles = static_cast<int32_t>((T + p.tile_m - 1) / p.tile_m);
+
+  Segment up[2] = {}, dn[2] = {};
+  up[0].a = x;
+  up[0].lda = D;
+  up[0].gather = r.sorted_pair;
+  up[0].topk = c.top_k;
+  up[0].b = w.w13;
+  up[0].b_stride = 2 * I * D;
+  up[0].b_scale = w.w13_scale;
+  up[0].s_stride = fp8 ? (2 * I / 128) * (D / 128) : 0;
+  up[0].n = static_cast<int32_t>(2 * I);
+  up[0].k = static_cast<int32_t>(D);
+  up[0].c = h;
+  up[0].ldc = I;
+  up[0].tile_row = r.tile_row;
+  up[0].tile_expert = r.tile_expert;
+  up[0].n_tiles_dev = r.n_tiles;
+  up[0].n_tiles_host = r.max_tiles;
+
+  dn[0].a = h;
+  dn[0].lda = I;
+  dn[0].b = w.w2;
+  dn[0].b_stride = D * I;
+  dn[0].b_scale = w.w2_scale;
+  dn[0].s_stride = fp8 ? (D / 128) * (I / 128) : 0;
+  dn[0].n = static_cast<int32_t>(D);
+  dn[0].k = static_cast<int32_t>(I);
+  dn[0].c = y;
+  dn[0].ldc = D;
+  dn[0].tile_row = r.tile_row;
+  dn[0].tile_expert = r.tile_expert;
+  dn[0].n_tiles_dev = r.n_tiles;
+  dn[0].n_tiles_host = r.max_tiles;
+
+  int nseg = 1;
+  if (shared) {
+    nseg = 2;
+    up[1].a = x;
+    up[1].lda = D;
+    up[1].a_rows = static_cast<int32_t>(T);
+    up[1].b = w.sw13;
+    up[1].b_scale = w.sw13_scale;
+    up[1].n = static_cast<int32_t>(2 * SI);
+    up[1].k = static_cast<int32_t>(D);
+    up[1].c = hs;
+    up[1].ldc = SI;
+    up[1].n_tiles_host = dense_tiles;
+
+    dn[1].a = hs;
+    dn[1].lda = SI;
+    dn[1].a_rows = static_cast<int32_t>(T);
+    dn[1].b = w.sw2;
+    dn[1].b_scale = w.sw2_scale;
+    dn[1].n = static_cast<int32_t>(D);
+    dn[1].k = static_cast<int32_t>(SI);
+    dn[1].c = z;
+    dn[1].ldc = D;
+    dn[1].n_tiles_host = dense_tiles;
+  }
+  hipError_t e;
+  switch (p.path) {
+    case PATH_F32:
+      e = launch_gemm_f32(up, nseg, p.tile_m, EPI_SWIGLU, st);
+      if (e == hipSuccess) e = launch_gemm_f32(dn, nseg, p.tile_m, EPI_STORE, st);
+      break;
+    case PATH_MFMA:
+      e = launch_gemm_mfma(up, nseg, p.tile_m, EPI_SWIGLU, false, st);
+      if (e == hipSuccess) e = launch_gemm_mfma(dn, nseg, p.tile_m, EPI_STORE, false, st);
+      break;
+    default:
+      e = launch_gemm_skinny(up, nseg, EPI_SWIGLU, fp8, false, st);
+      if (e == hipSuccess) e = launch_gemm_skinny(dn, nseg, EPI_STORE, fp8, false, st);
+      break;
+  }
+  if (e != hipSuccess) return device_fail(e, "expert FFN launch");
+  return ok();
+}
+
+moe_status check_weights(const moe_config &c, const moe_weights *w, bool need_shared) {
+  if (w == nullptr) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_NEED(w->w13, "w13");
+  MOE_NEED(w->w2, "w2");
+  const bool fp8 = c.weight_dtype == MOE_FP8_E4M3_B128;
+  if (fp8) {
+    if (w->w13_scale == nullptr || w->w2_scale == nullptr)
+      return fail(MOE_ERR_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+  }
+  if (need_shared && c.n_shared > 0) {
+    MOE_NEED(w->sw13, "sw13");
+    MOE_NEED(w->sw2, "sw2");
+    if (fp8 && (w->sw13_scale == nullptr || w->sw2_scale == nullptr))
+      return fail(MOE_ERR_INVALID_ARG, "fp8 shared weights need sw13_scale and sw2_scale");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_validate(const moe_config *cfg) {
+  MOE_TRY(check_cfg(cfg));
+  return ok();
+}
+
+moe_status moe_routing_size(const moe_config *cfg, int64_t T, size_t *bytes) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = routing_layout(*cfg, T).total;
+  return ok();
+}
+
+moe_status moe_routing_init(const moe_config *cfg, int64_t T, void *buf, size_t bytes,
+                            moe_routing *r) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (r == nullptr) return fail(MOE_ERR_INVALID_ARG, "routing struct is NULL");
+  if (buf == nullptr) return fail(MOE_ERR_INVALID_ARG, "routing buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(buf) % kAlign != 0)
+    return fail(MOE_ERR_INVALID_ARG, "routing buffer is not 256-byte aligned");
+  const RoutingLayout L = routing_layout(*cfg, T);
+  if (bytes < L.total) return fail(MOE_ERR_WORKSPACE, "routing buffer too small: %zu < %zu", bytes, L.total);
+  char *b = static_cast<char *>(buf);
+  r->tile_m = L.tile_m;
+  r->max_rows = static_cast<int32_t>(L.max_rows);
+  r->max_tiles = static_cast<int32_t>(L.max_tiles);
+  r->pad_ = 0;
+  r->counts = reinterpret_cast<int32_t *>(b + L.off_counts);
+  r->expert_off = reinterpret_cast<int32_t *>(b + L.off_expert_off);
+  r->sorted_pair = reinterpret_cast<int32_t *>(b + L.off_sorted);
+  r->pair_row = reinterpret_cast<int32_t *>(b + L.off_pair_row);
+  r->tile_expert = reinterpret_cast<int32_t *>(b + L.off_tile_expert);
+  r->tile_row = reinterpret_cast<int32_t *>(b + L.off_tile_row);
+  r->n_tiles = reinterpret_cast<int32_t *>(b + L.off_ntiles);
+  r->scratch = reinterpret_cast<int32_t *>(b + L.off_scratch);
+  return ok();
+}
+
+moe_status moe_workspace_size(const moe_config *cfg, int64_t T, size_t *bytes) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = workspace_layout(*cfg, T).total;
+  return ok();
+}
+
+const char *moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+moe_status moe_gate(const moe_config *cfg, int64_t T, const void *x, const void *w_gate,
+                    const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
+                    float *keys, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_bias(*cfg, bias));
+  MOE_NEED(x, "x");
+  MOE_NEED(w_gate, "w_gate");
+  if (logits == nullptr || topk_idx == nullptr || topk_w == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "logits, topk_idx and topk_w are required");
+  if (T == 0) return ok();
+  return do_gate(*cfg, T, x, w_gate, bias, logits, topk_idx, topk_w, keys,
+                 static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_config *cfg, int64_t T, const int32_t *topk_idx,
+                       const moe_routing *r, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (topk_idx == nullptr) return fail(MOE_ERR_INVALID_ARG, "topk_idx is NULL");
+  MOE_TRY(check_routing(*cfg, T, r));
+  if (T == 0) return ok();
+  const hipError_t e = launch_permute(*cfg, T, topk_idx, *r, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "permute launch");
+  return ok();
+}
+
+moe_status moe_expert_ffn(const moe_config *cfg, int64_t T, const void *x,
+                          const moe_routing *r, const moe_weights *w, void *h, void *y_pairs,
+                          void *hs, void *z, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_NEED(x, "x");
+  MOE_TRY(check_routing(*cfg, T, r));
+  MOE_TRY(check_weights(*cfg, w, z != nullptr));
+  MOE_NEED(h, "h");
+  MOE_NEED(y_pairs, "y_pairs");
+  if (z != nullptr && cfg->n_shared > 0) {
+    MOE_NEED(hs, "hs");
+    MOE_NEED(z, "z");
+  }
+  if (T == 0) return ok();
+  return do_ffn(*cfg, T, x, *r, *w, h, y_pairs, hs, z, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_config *cfg, int64_t T, const void *u, const void *z,
+                       const void *y_pairs, const moe_routing *r, const float *topk_w,
+                       void *out, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (cfg->add_residual) MOE_NEED(u, "u");
+  MOE_OPT(z, "z");
+  MOE_NEED(y_pairs, "y_pairs");
+  MOE_NEED(out, "out");
+  if (topk_w == nullptr) return fail(MOE_ERR_INVALID_ARG, "topk_w is NULL");
+  MOE_TRY(check_routing(*cfg, T, r));
+  if (T == 0) return ok();
+  const hipError_t e = launch_combine(*cfg, T, u, z, y_pairs, *r, topk_w, out,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "combine launch");
+  return ok();
+}
+
+moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                       void *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                       void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_NEED(x, "x");
+  MOE_NEED(out, "out");
+  if (out == x) return fail(MOE_ERR_INVALID_ARG, "out must not alias x");
+  MOE_TRY(check_weights(*cfg, w, true));
+  MOE_NEED(w->w_gate, "w_gate");
+  MOE_TRY(check_bias(*cfg, w->bias));
+  const moe_config &c = *cfg;
+  const WorkspaceLayout W = workspace_layout(c, T);
+  if (ws == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return fail(MOE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (ws_bytes < W.total) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, W.total);
+  if (T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *b = static_cast<char *>(ws);
+  float *logits = reinterpret_cast<float *>(b + W.off_logits);
+  int32_t *idx = topk_idx != nullptr ? topk_idx : reinterpret_cast<int32_t *>(b + W.off_idx);
+  float *wt = topk_w != nullptr ? topk_w : reinterpret_cast<float *>(b + W.off_w);
+  moe_routing r{};
+  MOE_TRY(moe_routing_init(cfg, T, b + W.off_routing, W.rl.total, &r));
+  MOE_TRY(do_gate(c, T, x, w->w_gate, w->bias, logits, idx, wt, nullptr, st));
+  hipError_t e = launch_permute(c, T, idx, r, st);
+  if (e != hipSuccess) return device_fail(e, "permute launch");
+  const bool shared = c.n_shared > 0;
+  void *h = b + W.off_h, *hs = b + W.off_hs, *y = b + W.off_y, *z = b + W.off_z;
+  MOE_TRY(do_ffn(c, T, x, r, *w, h, y, shared ? hs : nullptr, shared ? z : nullptr, st));
+  e = launch_combine(c, T, x, shared ? z : nullptr, y, r, wt, out, st);
+  if (e != hipSuccess) return device_fail(e, "combine launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Combine (DeepSeek-V3 notes page, "DeepSeekMoE" total-output equation):
+//   out[t] = u[t] + z[t] + sum_k w[t,k] * y[pair_row[t*K+k]]
+// One workgroup per token; every thread owns 16-byte column chunks and sums in
+// fp32 in a fixed order (u, z, then slots k = 0..K-1, which the gate emits in
+// ascending expert order), rounding once.  No atomics: the result is unique.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxK = 32;
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int K,
+                                                           const void *__restrict__ u,
+                                                           const void *__restrict__ z,
+                                                           const void *__restrict__ y,
+                                                           const int32_t *__restrict__ pair_row,
+                                                           const float *__restrict__ w,
+                                                           void *__restrict__ out, int residual) {
+  __shared__ int s_row[kMaxK];
+  __shared__ float s_w[kMaxK];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < K) {
+    s_row[threadIdx.x] = pair_row[t * K + threadIdx.x];
+    s_w[threadIdx.x] = w[t * K + threadIdx.x];
+  }
+  __syncthreads();
+  constexpr int V = BF16 ? 8 : 4;   // elements per 16-byte chunk
+  const int nchunks = D / V;
+  for (int c = threadIdx.x; c < nchunks; c += kThreads) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+    auto add_row = [&](const void *base, int64_t row, float scale, bool fma_mode) {
+      const u32x4_t v = reinterpret_cast<const u32x4_t *>(base)[(row * D) / V + c];
+      if (BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
+          acc[2 * i] = fma_mode ? fmaf(scale, lo, acc[2 * i]) : acc[2 * i] + lo;
+          acc[2 * i + 1] = fma_mode ? fmaf(scale, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float f = __uint_as_float(v[i]);
+          acc[i] = fma_mode ? fmaf(scale, f, acc[i]) : acc[i] + f;
+        }
+      }
+    };
+    if (residual) add_row(u, t, 1.0f, false);
+    if (z != nullptr) add_row(z, t, 1.0f, false);
+    for (int k = 0; k < K; ++k) {
+      const int row = s_row[k];
+      if (row >= 0) add_row(y, row, s_w[k], true);
+    }
+    u32x4_t o;
+    if (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+    }
+    reinterpret_cast<u32x4_t *>(out)[(t * D) / V + c] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_config &cfg, int64_t T, const void *u, const void *z,
+                          const void *y, const moe_routing &r, const float *w, void *out,
+                          hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(T)), block(kThreads);
+  if (cfg.act_dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, st, T, cfg.dim, cfg.top_k, u, z, y,
+                       r.pair_row, w, out, cfg.add_residual);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, st, T, cfg.dim, cfg.top_k, u, z, y,
+                       r.pair_row, w, out, cfg.add_residual);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,92 @@
+// Internal declarations shared by the HIP kernels of the MoE layer forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe355.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// ---- bf16 <-> fp32 -----------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// round-to-nearest-even fp32 -> bf16 bits (inputs are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// ---- GEMM segment: C[rows, N] (+)= A[rows, K] * B[N, K]^T for one group of rows
+// sharing a weight matrix.  A rows may be gathered: row r of a tile holds pair
+// p = sorted_pair[r] (p < 0: zero row) whose token is p / topk.
+struct Segment {
+  const void *a;          // A base (x, h, hs)
+  int64_t lda;            // elements
+  const int32_t *gather;  // sorted_pair (routed gate_up) or nullptr (rows are direct)
+  int32_t topk;           // pair -> token divisor when gathering
+  int32_t a_rows;         // rows valid in A when not gathering (dense segment), else unused
+  const void *b;          // B base of expert 0 (or the only matrix)
+  int64_t b_stride;       // elements between experts' matrices
+  const float *b_scale;   // fp8 block scales of expert 0, or nullptr
+  int64_t s_stride;       // floats between experts' scale tensors
+  int32_t n;              // B rows (output columns; 2*inter for gate_up)
+  int32_t k;              // reduction length
+  void *c;                // output base
+  int64_t ldc;            // elements
+  // tiles: routed segments read the tile lists written by moe_permute; dense
+  // segments cover rows [0, a_rows) in tiles of tile_m with expert 0.
+  const int32_t *tile_row;
+  const int32_t *tile_expert;
+  const int32_t *n_tiles_dev;  // nullptr -> dense
+  int32_t n_tiles_host;        // dense tile count, or capacity for routed
+};
+
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1 };
+
+// plan chosen for (cfg, T)
+enum Path { PATH_F32 = 0, PATH_MFMA = 1, PATH_SKINNY = 2 };
+struct Plan {
+  int path;
+  int tile_m;
+};
+
+// ---- launchers (each returns hipSuccess or the launch error) ----------------
+hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logits,
+                             const float *bias, int32_t *topk_idx, float *topk_w, float *keys,
+                             hipStream_t st);
+hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_idx,
+                          const moe_routing &r, hipStream_t st);
+hipError_t launch_combine(const moe_config &cfg, int64_t T, const void *u, const void *z,
+                          const void *y, const moe_routing &r, const float *w, void *out,
+                          hipStream_t st);
+
+// out_f32: C is fp32 (gate logits) instead of the act dtype
+hipError_t launch_gemm_f32(const Segment *segs, int nseg, int tile_m, Epilogue epi,
+                           hipStream_t st);
+hipError_t launch_gemm_mfma(const Segment *segs, int nseg, int tile_m, Epilogue epi,
+                            bool out_f32, hipStream_t st);
+hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool w_fp8,
+                              bool out_f32, hipStream_t st);
+
+constexpr int kMfmaTileM = 128;
+constexpr int kSkinnyTileM = 16;
+constexpr int kF32TileM = 64;
+
+}  // namespace moe

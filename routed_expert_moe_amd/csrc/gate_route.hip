@@ -1,0 +1,195 @@
+// Gate, steps 1b-5 (DeepSeek-V3 notes page, gate flow): scores from the fp32
+// logits, group-limited selection, global top-k, weights from the unbiased
+// scores.  One 64-lane wavefront per token; four tokens per workgroup.
+//
+// Selection is exact integer work on packed 64-bit keys
+//     (orderable(key) << 32) | (0xFFFFFFFF - expert)
+// so the maximum is unique and equal keys rank the lower expert first.  The
+// top-k runs as K rounds of a wavefront max reduction.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kMaxE = 512;
+
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0 ranks equal to +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off);
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off);
+    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void gate_route_kernel(
+    const float *__restrict__ logits, const float *__restrict__ bias, int64_t T, int E, int G,
+    int TG, int K, int softmax, int normalise, float route_scale, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, float *__restrict__ keys_out) {
+  __shared__ float s_key[kWaves][kMaxE];
+  __shared__ float s_score[kWaves][kMaxE];
+  __shared__ float s_w[kWaves][32];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (t >= T) return;  // uniform per wavefront; no workgroup barrier below
+
+  const float *lrow = logits + t * E;
+  float l[NPL], s[NPL], key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane + 64 * j;
+    l[j] = e < E ? lrow[e] : -INFINITY;
+  }
+
+  // step 1: scores and ranked keys
+  if (!softmax) {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + 64 * j;
+      s[j] = 1.0f / (1.0f + expf(-l[j]));
+      key[j] = bias != nullptr && e < E ? s[j] + bias[e] : s[j];
+    }
+  } else {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) m = fmaxf(m, l[j]);
+    m = wave_max_f32(m);
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + 64 * j;
+      s[j] = e < E ? expf(l[j] - m) : 0.0f;
+      sum += s[j];
+    }
+    sum = wave_sum_f32(sum);
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + 64 * j;
+      s[j] = s[j] / sum;
+      key[j] = bias != nullptr && e < E ? s[j] + bias[e] : l[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      s_key[wave][e] = key[j];
+      s_score[wave][e] = s[j];
+      if (keys_out != nullptr) keys_out[t * E + e] = key[j];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // steps 2-3: group scores (top-2 sum with a bias, else max), keep topk_groups
+  uint64_t keep = ~0ull;
+  const int gsz = E / G;
+  if (G > 1) {
+    float gs = -INFINITY;
+    if (lane < G) {
+      float b1 = -INFINITY, b2 = -INFINITY;
+      const float *gk = &s_key[wave][lane * gsz];
+      for (int i = 0; i < gsz; ++i) {
+        const float v = gk[i];
+        if (v > b1) {
+          b2 = b1;
+          b1 = v;
+        } else if (v > b2) {
+          b2 = v;
+        }
+      }
+      gs = bias != nullptr ? b1 + b2 : b1;
+    }
+    int rank = 0;
+    for (int g = 0; g < G; ++g) {
+      const float o = __shfl(gs, g);
+      rank += (o > gs) || (o == gs && g < lane);
+    }
+    keep = __ballot(lane < G && rank < TG);
+  }
+
+  // step 4: global top-k over the surviving experts
+  uint64_t pk[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane + 64 * j;
+    const bool on = e < E && ((keep >> (e / gsz)) & 1ull);
+    pk[j] = on ? ((static_cast<uint64_t>(orderable(key[j])) << 32) | (0xFFFFFFFFu - e)) : 0ull;
+  }
+  int mine = 0x7FFFFFFF;
+  for (int r = 0; r < K; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) best = pk[j] > best ? pk[j] : best;
+    best = wave_max_u64(best);
+    const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    if (lane == r) mine = e;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (pk[j] == best) pk[j] = 0ull;
+  }
+
+  // ascending expert order: lane r (< K) holds the r-th pick; place it by rank
+  int pos = 0;
+  for (int r = 0; r < K; ++r) pos += __shfl(mine, r) < mine;
+  // step 5: unbiased scores at the chosen experts, renormalised, scaled
+  float val = lane < K ? s_score[wave][mine] : 0.0f;
+  if (lane < K) s_w[wave][pos] = val;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  float scale = route_scale;
+  if (normalise) {
+    float tot = 0.0f;
+    for (int r = 0; r < K; ++r) tot += s_w[wave][r];  // ascending expert order
+    scale = route_scale / tot;
+  }
+  if (lane < K) {
+    topk_idx[t * K + pos] = mine;
+    topk_w[t * K + pos] = val * scale;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logits,
+                             const float *bias, int32_t *topk_idx, float *topk_w, float *keys,
+                             hipStream_t st) {
+  const int E = cfg.n_routed;
+  const int softmax = cfg.score_func == MOE_SCORE_SOFTMAX;
+  const int normalise = cfg.norm_topk >= 0 ? cfg.norm_topk : !softmax;
+  const dim3 grid(static_cast<unsigned>((T + kWaves - 1) / kWaves));
+  const dim3 block(64 * kWaves);
+#define MOE_ROUTE(NPL)                                                                       \
+  hipLaunchKernelGGL(gate_route_kernel<NPL>, grid, block, 0, st, logits, bias, T, E,          \
+                     cfg.n_groups, cfg.topk_groups, cfg.top_k, softmax, normalise,            \
+                     cfg.route_scale, topk_idx, topk_w, keys)
+  if (E <= 64) MOE_ROUTE(1);
+  else if (E <= 128) MOE_ROUTE(2);
+  else if (E <= 256) MOE_ROUTE(4);
+  else MOE_ROUTE(8);
+#undef MOE_ROUTE
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,142 @@
+"""The C ABI on the CPU: the library loads, exports every entry point its
+header declares, and validates arguments on the host before any launch (so
+every error path here runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from routed_expert_moe_amd import binding as B
+from routed_expert_moe_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe355.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = _declared()
+    assert set(names) >= {"moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(B.EXPORTED) == set(names)
+
+
+def test_struct_sizes_match_header_layout():
+    assert ctypes.sizeof(B.moe_config) == 13 * 4
+    assert ctypes.sizeof(B.moe_weights) == 10 * 8
+    assert ctypes.sizeof(B.moe_routing) == 16 + 8 * 8
+
+
+@pytest.mark.parametrize("shape", configs.ALL, ids=lambda s: s.name)
+def test_named_shapes_validate(shape):
+    B.moe_validate(B.config_of(shape))
+    assert B.moe_workspace_size(B.config_of(shape), shape.T) > 0
+    assert B.moe_routing_size(B.config_of(shape), shape.T) > 0
+
+
+def _cfg(**kw):
+    c = B.config_of(configs.TINY_F32)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_groups=3), B.MOE_ERR_INVALID_ARG),            # 16 % 3 != 0
+    (dict(topk_groups=0), B.MOE_ERR_INVALID_ARG),
+    (dict(topk_groups=5), B.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), B.MOE_ERR_INVALID_ARG),               # > topk_groups * group size
+    (dict(top_k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(route_scale=0.0), B.MOE_ERR_INVALID_ARG),
+    (dict(route_scale=float("nan")), B.MOE_ERR_INVALID_ARG),
+    (dict(route_scale=float("inf")), B.MOE_ERR_INVALID_ARG),
+    (dict(dim=0), B.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(score_func=7), B.MOE_ERR_INVALID_ARG),
+    (dict(norm_topk=2), B.MOE_ERR_INVALID_ARG),
+    (dict(add_residual=3), B.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=B.MOE_F32, weight_dtype=B.MOE_BF16), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=B.MOE_F32, weight_dtype=B.MOE_FP8_E4M3_B128), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=B.MOE_BF16, weight_dtype=B.MOE_FP8_E4M3_B128, inter_dim=192), B.MOE_ERR_UNSUPPORTED),
+    (dict(dim=260), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_routed=1024, n_groups=1, topk_groups=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_routed=64, n_groups=1, topk_groups=1, top_k=33), B.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_configs_rejected(kw, status):
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_validate(_cfg(**kw))
+    assert ei.value.status == status
+
+
+def test_entry_points_validate_before_launch():
+    """Every failure below is caught on the host; nothing is enqueued."""
+    c = _cfg()
+    L = B.lib()
+    fake = 1 << 20   # aligned, never dereferenced: validation fails first
+    # negative T
+    assert L.moe_gate(ctypes.byref(c), -1, fake, fake, None, fake, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    # NULL inputs / outputs
+    assert L.moe_gate(ctypes.byref(c), 4, None, fake, None, fake, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_gate(ctypes.byref(c), 4, fake, fake, None, None, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    # misaligned pointer
+    assert L.moe_gate(ctypes.byref(c), 4, fake + 2, fake, None, fake, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert b"aligned" in L.moe_last_error()
+    # bias with groups of one expert
+    c1 = _cfg(n_routed=4, n_groups=4, topk_groups=2, top_k=2)
+    assert L.moe_gate(ctypes.byref(c1), 4, fake, fake, fake, fake, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    # routing struct built for another T
+    r = B.moe_routing_init(c, 64, fake, B.moe_routing_size(c, 64))
+    assert L.moe_permute(ctypes.byref(c), 32, fake, ctypes.byref(r), None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(ctypes.byref(c), 32, fake, None, fake, ctypes.byref(r), fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    # workspace too small / NULL / misaligned
+    w = B.moe_weights(w_gate=fake, w13=fake, w2=fake, sw13=fake, sw2=fake)
+    need = B.moe_workspace_size(c, 64)
+    assert L.moe_forward(ctypes.byref(c), 64, fake, ctypes.byref(w), fake + 256, None, None, fake, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_forward(ctypes.byref(c), 64, fake, ctypes.byref(w), fake + 256, None, None, None, need, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(ctypes.byref(c), 64, fake, ctypes.byref(w), fake + 256, None, None, fake + 16, need, None) == B.MOE_ERR_INVALID_ARG
+    # out aliasing x
+    assert L.moe_forward(ctypes.byref(c), 64, fake, ctypes.byref(w), fake, None, None, fake, need, None) == B.MOE_ERR_INVALID_ARG
+    # missing shared weights when n_shared > 0
+    w2 = B.moe_weights(w_gate=fake, w13=fake, w2=fake)
+    assert L.moe_forward(ctypes.byref(c), 64, fake, ctypes.byref(w2), fake + 256, None, None, fake, need, None) == B.MOE_ERR_INVALID_ARG
+    # fp8 without scales
+    c8 = B.config_of(configs.V3_DECODE_FP8)
+    need8 = B.moe_workspace_size(c8, 8)
+    assert L.moe_forward(ctypes.byref(c8), 8, fake, ctypes.byref(w), fake + 256, None, None, fake, need8, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_T_zero_is_a_no_op():
+    c = _cfg()
+    L = B.lib()
+    fake = 1 << 20
+    assert L.moe_gate(ctypes.byref(c), 0, fake, fake, None, fake, fake, fake, None, None) == B.MOE_OK
+    w = B.moe_weights(w_gate=fake, w13=fake, w2=fake, sw13=fake, sw2=fake)
+    need = B.moe_workspace_size(c, 0)
+    assert L.moe_forward(ctypes.byref(c), 0, fake, ctypes.byref(w), fake + 256, None, None, fake, need, None) == B.MOE_OK
+    assert L.moe_last_error() == b""
+
+
+def test_routing_layout_is_aligned_and_disjoint():
+    for shape in configs.ALL:
+        c = B.config_of(shape)
+        n = B.moe_routing_size(c, shape.T)
+        base = 1 << 30
+        r = B.moe_routing_init(c, shape.T, base, n)
+        P = shape.T * shape.top_k
+        spans = sorted([(r.counts, 4 * shape.n_routed), (r.expert_off, 4 * (shape.n_routed + 1)),
+                        (r.sorted_pair, 4 * r.max_rows), (r.pair_row, 4 * P),
+                        (r.tile_expert, 4 * r.max_tiles), (r.tile_row, 4 * r.max_tiles),
+                        (r.n_tiles, 4), (r.scratch, 4)])
+        for (a, la), (b, _) in zip(spans, spans[1:]):
+            assert a % 256 == 0 and a + la <= b
+        assert spans[-1][0] < base + n
+        assert r.max_rows % r.tile_m == 0 and r.max_rows >= P + shape.n_routed * (r.tile_m - 1)
+        assert r.max_tiles * r.tile_m == r.max_rows

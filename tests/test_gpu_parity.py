@@ -1,0 +1,339 @@
+"""GPU parity: every step of the HIP path against the float64 CPU oracle.
+
+Expert indices are compared bit-exactly under the certification protocol in
+tests/parity.py; floating outputs within max|err| / max|ref| <= 1e-5 (fp32
+layers), 2e-2 (bf16) and 6e-2 (fp8 weights), on the layer output h' and on
+h' - u.  Small shapes are checked on every token; the full-size shapes on the
+gate of every token and the output of a seeded token sample.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle_bridge import bias_f64, expert_fn, run_oracle, shared_pair, spec_of, to_f64
+from parity import TOL, certify, rel_err, run_gate, say
+from routed_expert_moe_amd import binding as B
+from routed_expert_moe_amd import configs, synth
+from routed_expert_moe_amd.configs import LayerShape
+
+pytestmark = pytest.mark.gpu
+
+C = configs
+SHAPES = {
+    "tiny_f32": C.TINY_F32,
+    "tiny_f32_T37": C.TINY_F32.with_(name="tiny_f32_T37", T=37),
+    "tiny_f32_T1": C.TINY_F32.with_(name="tiny_f32_T1", T=1),
+    "f32_softmax_noshared": LayerShape(
+        name="f32_softmax_noshared", T=100, dim=64, n_routed=8, n_groups=1, topk_groups=1,
+        top_k=2, n_shared=0, inter_dim=40, score="softmax", route_scale=1.0, act="f32",
+        weight="f32", seed=21),
+    "v2lite_full": C.V2_LITE_BF16,
+    "mfma_groups_ragged": LayerShape(
+        name="mfma_groups_ragged", T=777, dim=384, n_routed=32, n_groups=4, topk_groups=2,
+        top_k=4, n_shared=1, inter_dim=320, score="sigmoid", route_scale=2.5, act="bf16",
+        weight="bf16", seed=11, bias_range=0.1),
+    "mfma_ktail_softmax": LayerShape(
+        name="mfma_ktail_softmax", T=301, dim=200, n_routed=8, n_groups=1, topk_groups=1,
+        top_k=2, n_shared=2, inter_dim=136, score="softmax", route_scale=1.0, act="bf16",
+        weight="bf16", seed=12),
+    "skinny_bf16": LayerShape(
+        name="skinny_bf16", T=40, dim=512, n_routed=64, n_groups=8, topk_groups=4, top_k=6,
+        n_shared=1, inter_dim=256, score="sigmoid", route_scale=2.5, act="bf16", weight="bf16",
+        seed=13, bias_range=0.05),
+    "fp8_small": LayerShape(
+        name="fp8_small", T=24, dim=256, n_routed=32, n_groups=4, topk_groups=2, top_k=4,
+        n_shared=1, inter_dim=256, score="sigmoid", route_scale=2.5, act="bf16", weight="fp8",
+        seed=14, bias_range=0.05),
+    "fp8_T1": LayerShape(
+        name="fp8_T1", T=1, dim=256, n_routed=32, n_groups=4, topk_groups=2, top_k=4,
+        n_shared=1, inter_dim=256, score="sigmoid", route_scale=2.5, act="bf16", weight="fp8",
+        seed=15, bias_range=0.05),
+    "v3_decode_fp8": C.V3_DECODE_FP8,
+}
+# full-size shapes: gate on every token, outputs on a token sample
+LARGE = {"v2_T4096": (C.V2_BF16, 12), "v3_prefill_T8192": (C.V3_PREFILL_BF16, 8)}
+
+_cache = {}
+
+
+def layer_for(shape: LayerShape):
+    if shape.name not in _cache:
+        if len(_cache) > 2:
+            _cache.clear()
+            torch.cuda.empty_cache()
+        say(f"[make_layer] {shape.name} T={shape.T} seed={shape.seed}")
+        dev = "cpu" if shape.T * shape.dim * shape.n_routed < 2 ** 27 else "cuda"
+        lay = synth.make_layer(shape, device=dev)
+        if dev == "cpu":
+            for f in ("x", "w_gate", "bias", "w13", "w2", "sw13", "sw2", "w13_scale", "w2_scale",
+                      "sw13_scale", "sw2_scale"):
+                t = getattr(lay, f)
+                if t is not None:
+                    setattr(lay, f, t.cuda())
+        _cache[shape.name] = lay
+    return _cache[shape.name]
+
+
+def check_gate(layer):
+    shape = layer.shape
+    say(f"[moe_gate] {shape.name}")
+    logits, keys, idx, w = run_gate(layer)
+    g = oracle.gate(to_f64(layer.x), to_f64(layer.w_gate), bias_f64(layer), spec_of(shape))
+    # logits: fp32 accumulation of exact products
+    assert rel_err(logits, g.logits) < 1e-5
+    cert, eps = certify(layer, idx, keys, g)
+    say(f"  eps={eps:.3g} uncertified={int((~cert).sum())}/{len(cert)}")
+    assert (~cert).mean() < 0.02
+    # weights on certified tokens; sum to route_scale on the sigmoid path
+    assert np.max(np.abs(w[cert] - g.w[cert])) <= 1e-5 * shape.route_scale
+    if shape.score == "sigmoid":
+        assert np.allclose(w.sum(axis=1), shape.route_scale, rtol=1e-5, atol=0)
+    assert (np.diff(idx, axis=1) > 0).all()
+    if shape.n_groups > 1:
+        gsz = shape.n_routed // shape.n_groups
+        assert all(len(set((row // gsz).tolist())) <= shape.topk_groups for row in idx)
+    return idx, w, cert
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_gate_parity(name):
+    check_gate(layer_for(SHAPES[name]))
+
+
+@pytest.mark.parametrize("name", list(LARGE))
+def test_gate_parity_full_size(name):
+    check_gate(layer_for(LARGE[name][0]))
+
+
+def run_forward(layer, x=None):
+    x = layer.x if x is None else x
+    mod = B.MoELayer(layer, T_max=x.shape[0])
+    T, K = x.shape[0], layer.shape.top_k
+    idx = torch.empty(T, K, dtype=torch.int32, device=x.device)
+    w = torch.empty(T, K, dtype=torch.float32, device=x.device)
+    out = mod.forward(x, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    return out, idx.cpu().numpy().astype(np.int64), w.cpu().numpy()
+
+
+def check_forward(layer, tokens=None):
+    shape = layer.shape
+    say(f"[moe_forward] {shape.name} T={layer.x.shape[0]} sample={None if tokens is None else len(tokens)}")
+    out, idx, w = run_forward(layer)
+    ref, g = run_oracle(layer, tokens=tokens, force_idx=idx)
+    # the GPU's selection must be certified-equal to the oracle's own (checked in the gate test);
+    # here the values are compared on the GPU's selection
+    got = to_f64(out)
+    u = to_f64(layer.x)
+    if tokens is not None:
+        got, u = got[tokens], u[tokens]
+    tol = TOL[shape.weight if shape.weight == "fp8" else shape.act]
+    e_out = rel_err(got, ref)
+    e_ffn = rel_err(got - u, ref - u) if shape.add_residual else e_out
+    say(f"  rel err h'={e_out:.3g}  h'-u={e_ffn:.3g}  tol={tol}")
+    assert e_out <= tol and e_ffn <= tol
+    assert np.all(np.isfinite(got))
+    return out
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_forward_parity(name):
+    check_forward(layer_for(SHAPES[name]))
+
+
+@pytest.mark.parametrize("name", list(LARGE))
+def test_forward_parity_full_size_sampled(name):
+    shape, n = LARGE[name]
+    rng = np.random.default_rng(shape.seed + 100)
+    toks = np.sort(rng.choice(shape.T, size=n, replace=False))
+    toks[-1] = shape.T - 1           # the last (ragged-tail) token
+    check_forward(layer_for(shape), tokens=toks)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "mfma_groups_ragged", "fp8_small", "v2lite_full"])
+def test_steps_equal_forward_and_deterministic(name):
+    """gate -> permute -> expert_ffn -> combine == moe_forward, bit for bit; reruns identical."""
+    layer = layer_for(SHAPES[name])
+    shape = layer.shape
+    say(f"[steps] {name}")
+    cfg = B.config_of(shape)
+    x = layer.x
+    T, E, K, D, I = x.shape[0], shape.n_routed, shape.top_k, shape.dim, shape.inter_dim
+    SI = shape.n_shared * I
+    dev, act = x.device, x.dtype
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+    w = torch.empty(T, K, dtype=torch.float32, device=dev)
+    B.moe_gate(cfg, T, x, layer.w_gate, layer.bias, logits, idx, w)
+    r = B.make_routing(cfg, T)
+    B.moe_permute(cfg, T, idx, r)
+    h = torch.empty(r.struct.max_rows, I, dtype=act, device=dev)
+    y = torch.empty(r.struct.max_rows, D, dtype=act, device=dev)
+    hs = torch.empty(T, max(SI, 1), dtype=act, device=dev) if SI else None
+    z = torch.empty(T, D, dtype=act, device=dev) if SI else None
+    B.moe_expert_ffn(cfg, T, x, r, B.weights_of(layer), h, y, hs, z)
+    out = torch.empty_like(x)
+    B.moe_combine(cfg, T, x, z, y, r, w, out)
+    out2, idx2, w2 = run_forward(layer)
+    out3, _, _ = run_forward(layer)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(out2, out3)
+    assert np.array_equal(idx.cpu().numpy(), idx2) and np.array_equal(w.cpu().numpy(), w2)
+
+
+def _permute_expect(idx: np.ndarray, E: int, TM: int):
+    P = idx.size
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E)
+    padded = (counts + TM - 1) // TM * TM
+    off = np.concatenate([[0], np.cumsum(padded)])
+    order = np.argsort(np.where(valid, flat, E), kind="stable")[: int(valid.sum())]
+    return counts, off, order
+
+
+def check_permute(shape: LayerShape, idx_np: np.ndarray):
+    cfg = B.config_of(shape)
+    T, K, E = idx_np.shape[0], shape.top_k, shape.n_routed
+    say(f"[moe_permute] {shape.name} T={T} K={K} E={E}")
+    r = B.make_routing(cfg, T)
+    idx = torch.from_numpy(idx_np.astype(np.int32)).cuda()
+    B.moe_permute(cfg, T, idx, r)
+    torch.cuda.synchronize()
+    TM = r.struct.tile_m
+    counts, off, order = _permute_expect(idx_np, E, TM)
+    assert np.array_equal(r.counts.cpu().numpy(), counts)
+    assert np.array_equal(r.expert_off.cpu().numpy(), off)
+    sp = r.sorted_pair.cpu().numpy()[: off[-1]]
+    got_order = sp[sp >= 0]
+    assert np.array_equal(got_order, order)                       # stable expert sort
+    pr = r.pair_row.cpu().numpy()
+    flat = idx_np.reshape(-1)
+    for e in range(E):
+        seg = sp[off[e]: off[e + 1]]
+        assert np.all(seg[: counts[e]] >= 0) and np.all(seg[counts[e]:] == -1)
+        assert np.all(flat[seg[: counts[e]]] == e)
+    valid = (flat >= 0) & (flat < E)
+    assert np.array_equal(sp[pr[valid]], np.nonzero(valid)[0])     # pair_row inverts sorted_pair
+    assert np.all(pr[~valid] == -1)
+    nt = int(r.n_tiles.cpu().item())
+    assert nt == off[-1] // TM
+    te, tr = r.tile_expert.cpu().numpy()[:nt], r.tile_row.cpu().numpy()[:nt]
+    assert np.array_equal(tr, np.arange(nt) * TM)
+    assert np.array_equal(te, np.searchsorted(off, tr, side="right") - 1)
+
+
+@pytest.mark.parametrize("case", ["random", "one_expert", "empty_experts", "T1", "large_ragged",
+                                  "dropped_entries", "max_E"])
+def test_permute_cases(case):
+    rng = np.random.default_rng(7)
+    shape = C.V3_PREFILL_BF16.with_(name=f"perm_{case}")
+    if case == "random":
+        T = 1000
+        idx = np.sort(np.stack([rng.choice(256, 8, replace=False) for _ in range(T)]), axis=1)
+    elif case == "one_expert":
+        shape = C.TINY_F32.with_(name="perm_one", top_k=1, n_groups=1, topk_groups=1)
+        idx = np.zeros((3000, 1), np.int64)
+    elif case == "empty_experts":
+        T = 700
+        idx = np.sort(np.stack([rng.choice(20, 8, replace=False) for _ in range(T)]), axis=1)
+    elif case == "T1":
+        idx = np.arange(8)[None, :] * 3
+    elif case == "large_ragged":
+        T = 8191
+        idx = np.sort(np.stack([rng.choice(256, 8, replace=False) for _ in range(T)]), axis=1)
+    elif case == "dropped_entries":
+        T = 300
+        idx = np.sort(np.stack([rng.choice(256, 8, replace=False) for _ in range(T)]), axis=1)
+        idx[::7, 3] = -1
+        idx[::11, 5] = 999
+    else:  # max_E
+        shape = LayerShape(name="perm_maxE", T=600, dim=256, n_routed=512, n_groups=1, topk_groups=1,
+                           top_k=32, n_shared=0, inter_dim=128, score="softmax", route_scale=1.0,
+                           act="bf16", weight="bf16")
+        idx = np.sort(np.stack([rng.choice(512, 32, replace=False) for _ in range(600)]), axis=1)
+    check_permute(shape, idx)
+
+
+def test_combine_one_hot_selects_rows():
+    """With one-hot weights the combine returns u + z + the selected row (one rounding)."""
+    layer = layer_for(SHAPES["mfma_groups_ragged"])
+    shape = layer.shape
+    cfg = B.config_of(shape)
+    T, K, D = shape.T, shape.top_k, shape.dim
+    say("[moe_combine] one-hot")
+    logits = torch.empty(T, shape.n_routed, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    B.moe_gate(cfg, T, layer.x, layer.w_gate, layer.bias, logits, idx, w)
+    r = B.make_routing(cfg, T)
+    B.moe_permute(cfg, T, idx, r)
+    g = torch.Generator(device="cpu").manual_seed(3)
+    y = torch.randn(r.struct.max_rows, D, generator=g).to(torch.bfloat16).cuda()
+    z = torch.randn(T, D, generator=g).to(torch.bfloat16).cuda()
+    pick = torch.randint(0, K, (T,), generator=g)
+    onehot = torch.zeros(T, K, dtype=torch.float32)
+    onehot[torch.arange(T), pick] = 1.0
+    out = torch.empty_like(layer.x)
+    B.moe_combine(cfg, T, layer.x, z, y, r, onehot.cuda(), out)
+    torch.cuda.synchronize()
+    rows = r.pair_row.cpu().numpy().reshape(T, K)[np.arange(T), pick.numpy()]
+    ref = to_f64(layer.x) + to_f64(z) + to_f64(y)[rows]
+    got = to_f64(out)
+    assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-3)) <= 2.0 ** -8
+    # zero weights and no residual: exactly z
+    cfg.add_residual = 0
+    B.moe_combine(cfg, T, None, z, y, r, torch.zeros(T, K, device="cuda"), out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, z)
+
+
+def test_imbalanced_routing_many_tiles():
+    """A bias that sends every token to the same four experts: one expert holds T rows."""
+    shape = SHAPES["mfma_groups_ragged"].with_(name="imbalanced", T=1500, seed=31)
+    layer = synth.make_layer(shape, device="cuda")
+    b = torch.full((shape.n_routed,), -0.5, device="cuda")
+    b[:4] = 5.0
+    layer.bias = b
+    out, idx, w = run_forward(layer)
+    assert (idx == np.arange(4)).all()
+    ref, _ = run_oracle(layer, force_idx=idx)
+    assert rel_err(to_f64(out), ref) <= TOL["bf16"]
+
+
+def test_expert_rows_full_size_v3():
+    """y_pairs rows and the shared output z at the V3 prefill size, against the oracle FFN."""
+    layer = layer_for(C.V3_PREFILL_BF16)
+    shape = layer.shape
+    cfg = B.config_of(shape)
+    T, K, D, I = shape.T, shape.top_k, shape.dim, shape.inter_dim
+    say("[moe_expert_ffn] v3 full size rows")
+    logits = torch.empty(T, shape.n_routed, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    B.moe_gate(cfg, T, layer.x, layer.w_gate, layer.bias, logits, idx, w)
+    r = B.make_routing(cfg, T)
+    B.moe_permute(cfg, T, idx, r)
+    h = torch.empty(r.struct.max_rows, I, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(r.struct.max_rows, D, dtype=torch.bfloat16, device="cuda")
+    hs = torch.empty(T, I, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
+    B.moe_expert_ffn(cfg, T, layer.x, r, B.weights_of(layer), h, y, hs, z)
+    torch.cuda.synchronize()
+    counts = r.counts.cpu().numpy()
+    off = r.expert_off.cpu().numpy()
+    sp = r.sorted_pair.cpu().numpy()
+    # the busiest expert (several tiles) and two others, first/last rows of each
+    used = np.nonzero(counts > 0)[0]
+    experts = [int(np.argmax(counts)), int(used[np.argmin(counts[used])]), int(used[len(used) // 2])]
+    get = expert_fn(layer)
+    x64 = to_f64(layer.x)
+    for e in experts:
+        rows = [off[e], off[e] + counts[e] - 1, off[e] + counts[e] // 2]
+        toks = sp[rows] // K
+        ref = oracle.swiglu_ffn(x64[toks], *get(e))
+        assert rel_err(to_f64(y[rows]), ref) <= TOL["bf16"], e
+    toks = np.array([0, 1, T // 2, T - 1])
+    ref = oracle.swiglu_ffn(x64[toks], *shared_pair(layer))
+    assert rel_err(to_f64(z[toks]), ref) <= TOL["bf16"]
