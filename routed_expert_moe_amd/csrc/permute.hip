@@ -133,8 +133,9 @@ __device__ void scan_all(const PermArgs &a, int *s_pad) {
   }
 }
 
-// phase 3 for pairs [p0, p1)
+// phase 3 for pairs [p0, min(p1, P))
 __device__ void scatter_range(const PermArgs &a, int64_t p0, int64_t p1, int stride) {
+  if (p1 > a.P) p1 = a.P;
   for (int64_t p = p0; p < p1; p += stride) {
     const int e = expert_of(a, p);
     if (e < 0) {
