@@ -1,0 +1,235 @@
+"""Benchmark: forward pass of one DeepSeekMoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole layer (gate, dispatch, routed expert FFNs,
+shared expert, combine) over one batch of synthetic tokens already resident
+in HBM.  The headline workload is the V3-shaped prefill layer (T=8192, dim
+7168, 256 routed experts in 8 groups keep 4, top-8, 1 shared, inter 2048,
+bf16); the 8-token fp8 decode step of the same layer is reported beside it.
+Prints one JSON line.  Random-init weights of the layer's architecture and
+x ~ N(0,1), as described in synth.py.
+
+roofline: the dominant kernel is the gate/up grouped GEMM (moe_expert_up);
+its duration comes from HIP events recorded around it on the stream it runs
+on, inside the timed region.  Its algorithmic work per launch is
+2*T*K*(2I)*D + 2*T*(2*S*I)*D flops and the bytes of the touched experts'
+W1/W3 (plus block scales), the shared W1/W3, x and the written h.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=0, help="default: 10x --steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+class Pass:
+    """Device buffers for one layer and the step sequence of the hot path."""
+
+    def __init__(self, layer):
+        import torch
+        from routed_expert_moe_amd import binding as B
+        self.B = B
+        self.layer = layer
+        s = layer.shape
+        self.cfg = B.config_of(s)
+        B.moe_validate(self.cfg)
+        self.w = B.weights_of(layer)
+        T, E, K, D, I, S = s.T, s.n_routed, s.top_k, s.dim, s.inter_dim, s.n_shared
+        dev, act = layer.x.device, layer.x.dtype
+        self.T = T
+        self.logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+        self.tw = torch.empty(T, K, dtype=torch.float32, device=dev)
+        self.r = B.make_routing(self.cfg, T)
+        R = self.r.struct.max_rows
+        self.h = torch.empty(R, I, dtype=act, device=dev)
+        self.y = torch.empty(R, D, dtype=act, device=dev)
+        self.hs = torch.empty(T, S * I, dtype=act, device=dev) if S else None
+        self.z = torch.empty(T, D, dtype=act, device=dev) if S else None
+        self.out = torch.empty(T, D, dtype=act, device=dev)
+
+    def step(self, ev_up=None):
+        B, L = self.B, self.layer
+        B.moe_gate(self.cfg, self.T, L.x, L.w_gate, L.bias, self.logits, self.idx, self.tw)
+        B.moe_permute(self.cfg, self.T, self.idx, self.r)
+        if ev_up is not None:
+            ev_up[0].record()
+        B.moe_expert_up(self.cfg, self.T, L.x, self.r, self.w, self.h, self.hs)
+        if ev_up is not None:
+            ev_up[1].record()
+        B.moe_expert_down(self.cfg, self.T, self.r, self.w, self.h, self.hs, self.y, self.z)
+        B.moe_combine(self.cfg, self.T, L.x, self.z, self.y, self.r, self.tw, self.out)
+
+
+def work_figures(layer, counts):
+    """Algorithmic flops / bytes of the layer and of the gate/up kernel for the actual routing."""
+    s = layer.shape
+    T, E, K, D, I, S = s.T, s.n_routed, s.top_k, s.dim, s.inter_dim, s.n_shared
+    P = T * K
+    ab = 2 if s.act == "bf16" else 4
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[s.weight]
+    touched = int((counts > 0).sum())
+    w13_e = 2 * I * D * wb + (2 * I // 128) * (D // 128) * 4 * (s.weight == "fp8")
+    w2_e = D * I * wb + (D // 128) * (I // 128) * 4 * (s.weight == "fp8")
+    sw13 = 2 * S * I * D * wb + (2 * S * I // 128) * (D // 128) * 4 * (s.weight == "fp8") if S else 0
+    sw2 = D * S * I * wb + (D // 128) * (S * I // 128) * 4 * (s.weight == "fp8") if S else 0
+    flops_up = 2 * P * 2 * I * D + 2 * T * 2 * S * I * D
+    bytes_up = touched * w13_e + sw13 + T * D * ab + P * I * ab + T * S * I * ab
+    flops_layer = 2 * T * E * D + 2 * P * 3 * I * D + 2 * T * 3 * S * I * D
+    bytes_layer = touched * (w13_e + w2_e) + sw13 + sw2 + E * D * ab + 2 * T * D * ab
+    return dict(touched=touched, flops_up=flops_up, bytes_up=bytes_up, flops_layer=flops_layer,
+                bytes_layer=bytes_layer)
+
+
+def time_pass(p: Pass, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        p.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        p.step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    up_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return total_ms, up_ms, wall
+
+
+def cpu_baseline(layer, n_tokens: int):
+    """The float64 oracle on the first n_tokens tokens of the same workload, on host cores."""
+    import numpy as np
+    import threadpoolctl
+    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
+    import oracle
+    from oracle_bridge import bias_f64, expert_fn, shared_pair, spec_of, to_f64
+    x = to_f64(layer.x[:n_tokens])
+    wg = to_f64(layer.w_gate)
+    b = bias_f64(layer)
+    shared = shared_pair(layer)
+    t0 = time.perf_counter()
+    oracle.moe_layer(x, wg, b, expert_fn(layer), shared, spec_of(layer.shape))
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"first {n_tokens} tokens of the {layer.shape.name} workload, whole layer "
+                       f"(gate, {layer.shape.top_k} routed + shared SwiGLU experts, combine) in "
+                       f"float64; expert weights decoded from device copies inside the timed call; "
+                       f"{dt:.1f} s")}
+
+
+def copy_probe(mib: int):
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs the single-GPU layer forward only; --gpus {args.gpus} is not supported "
+              f"(no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+    from routed_expert_moe_amd import binding as B
+    from routed_expert_moe_amd import configs, synth
+    B.lib()
+
+    # ---- prefill: the headline workload
+    shape = configs.V3_PREFILL_BF16
+    layer = synth.make_layer(shape, device="cuda")
+    p = Pass(layer)
+    total_ms, up_ms, wall = time_pass(p, args.steps, args.warmup)
+    counts = p.r.counts.cpu().numpy()
+    fig = work_figures(layer, counts)
+    ms = total_ms / args.steps
+    tok_s = shape.T * args.steps / (total_ms / 1e3)
+    up_tflops = fig["flops_up"] / (up_ms / 1e3) / 1e12
+    res = {
+        "metric": "MoE-layer tokens/s + % MFMA peak (prefill), % HBM GB/s (decode), 1 MI355X",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
+        "config": {"workload": shape.name, "T": shape.T, "dim": shape.dim, "n_routed": shape.n_routed,
+                   "n_groups": shape.n_groups, "topk_groups": shape.topk_groups, "top_k": shape.top_k,
+                   "n_shared": shape.n_shared, "inter_dim": shape.inter_dim, "score": shape.score,
+                   "route_scale": shape.route_scale, "experts_touched": fig["touched"]},
+        "layer": {"tflops": fig["flops_layer"] / (ms / 1e3) / 1e12,
+                  "mfma_frac": fig["flops_layer"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "gbs": fig["bytes_layer"] / (ms / 1e3) / 1e9,
+                  "hbm_frac": fig["bytes_layer"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "roofline": {"kernel": "moe_expert_up (gate/up grouped GEMM + SwiGLU)", "bound": "mfma",
+                     "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": up_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "avg_launch_ms": up_ms, "algorithmic_flops": fig["flops_up"],
+                     "algorithmic_bytes": fig["bytes_up"]},
+        "wall_s": wall,
+    }
+    del p
+    torch.cuda.empty_cache()
+
+    # ---- decode: 8 tokens, fp8 expert weights
+    dshape = configs.V3_DECODE_FP8
+    dlayer = synth.make_layer(dshape, device="cuda")
+    dp = Pass(dlayer)
+    dsteps = args.decode_steps or 10 * args.steps
+    dtotal_ms, dup_ms, _ = time_pass(dp, dsteps, max(args.warmup, 3))
+    dfig = work_figures(dlayer, dp.r.counts.cpu().numpy())
+    dms = dtotal_ms / dsteps
+    up_gbs = dfig["bytes_up"] / (dup_ms / 1e3) / 1e9
+    res["decode"] = {
+        "workload": dshape.name, "T": dshape.T, "dtype": "fp8-e4m3 weights (128x128 fp32 scales), bf16 act",
+        "steps": dsteps, "ms_per_step": dms, "tokens_per_s": dshape.T * dsteps / (dtotal_ms / 1e3),
+        "experts_touched": dfig["touched"],
+        "layer_gbs": dfig["bytes_layer"] / (dms / 1e3) / 1e9,
+        "layer_hbm_frac": dfig["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": {"kernel": "moe_expert_up (fp8 weight-streaming gate/up + SwiGLU)", "bound": "hbm",
+                     "achieved": up_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": up_gbs / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": dup_ms,
+                     "algorithmic_bytes": dfig["bytes_up"]},
+    }
+    del dp, dlayer
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(layer, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -102,8 +102,8 @@ typedef struct moe_weights {
  * Build it with moe_routing_init over one caller buffer of moe_routing_size bytes. */
 typedef struct moe_routing {
   int32_t tile_m;        /* host: rows per expert tile (chosen by the library for (cfg, T)) */
-  int32_t max_rows;      /* host: capacity in rows = T*K + E*(tile_m-1) (rounded up) */
-  int32_t max_tiles;     /* host: capacity of the tile lists = ceil(T*K/tile_m) + E */
+  int32_t max_rows;      /* host: capacity in rows = T*K + E*(tile_m-1), rounded up to tile_m */
+  int32_t max_tiles;     /* host: capacity of the tile lists = max_rows / tile_m */
   int32_t pad_;
   int32_t *counts;       /* [E]          pairs routed to each expert */
   int32_t *expert_off;   /* [E+1]        first row of each expert (multiples of tile_m);
@@ -123,7 +123,7 @@ typedef struct moe_routing {
  * 1 <= top_k <= topk_groups*E/G, group size >= 2 when a bias makes the group
  * score a top-2 sum (checked at call time), route_scale finite and > 0,
  * dims > 0.  Returns MOE_ERR_UNSUPPORTED for valid layers outside the
- * kernels' limits: E > 512, top_k > 32, G > 32, dtype pairs other than
+ * kernels' limits: E > 512, top_k > 32, G > 64, dtype pairs other than
  * (F32,F32), (BF16,BF16), (BF16,FP8); D or I not a multiple of 8 (of 128 for fp8). */
 moe_status moe_validate(const moe_config *cfg);
 
@@ -160,7 +160,8 @@ moe_status moe_gate(const moe_config *cfg, int64_t T, const void *x, const void 
 /* Dispatch (replaces the per-expert gather of the notes page's MoE forward,
  * step 2): histogram of experts over the T*K pairs, exclusive scan of the
  * padded counts, stable scatter into expert-sorted rows, tile lists.
- *   topk_idx [T, K] int32 (each entry in [0, E));  r from moe_routing_init. */
+ *   topk_idx [T, K] int32;  r from moe_routing_init.  Entries outside [0, E)
+ *   are dropped: they get no row and pair_row = -1. */
 moe_status moe_permute(const moe_config *cfg, int64_t T, const int32_t *topk_idx,
                        const moe_routing *r, void *stream);
 
@@ -176,10 +177,22 @@ moe_status moe_expert_ffn(const moe_config *cfg, int64_t T, const void *x,
                           const moe_routing *r, const moe_weights *w, void *h, void *y_pairs,
                           void *hs, void *z, void *stream);
 
+/* The two halves of moe_expert_ffn, for callers that schedule or time them
+ * separately (same arguments and outputs as above):
+ *   moe_expert_up:   h (and hs when hs != NULL) from x
+ *   moe_expert_down: y_pairs from h (and z from hs when both are non-NULL) */
+moe_status moe_expert_up(const moe_config *cfg, int64_t T, const void *x, const moe_routing *r,
+                         const moe_weights *w, void *h, void *hs, void *stream);
+moe_status moe_expert_down(const moe_config *cfg, int64_t T, const moe_routing *r,
+                           const moe_weights *w, const void *h, const void *hs, void *y_pairs,
+                           void *z, void *stream);
+
 /* Combine (total-output equation): for every token t
  *   out[t] = (add_residual ? u[t] : 0) + (z ? z[t] : 0)
- *            + sum over k in ascending expert order of topk_w[t,k] * y_pairs[pair_row[t*K+k]]
- * summed in fp32 in exactly that order, rounded once to the act dtype.
+ *            + sum over slots k = 0..K-1 of topk_w[t,k] * y_pairs[pair_row[t*K+k]]
+ * summed in fp32 in exactly that order (the gate emits slots in ascending
+ * expert order), rounded once to the act dtype.  Pairs that moe_permute
+ * dropped (expert index outside [0, E)) contribute nothing.
  *   u [T, D], z [T, D] or NULL, out [T, D]: act dtype;  topk_w [T, K] fp32. */
 moe_status moe_combine(const moe_config *cfg, int64_t T, const void *u, const void *z,
                        const void *y_pairs, const moe_routing *r, const float *topk_w,

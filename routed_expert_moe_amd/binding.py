@@ -61,7 +61,7 @@ class moe_routing(ctypes.Structure):
 
 EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspace_size",
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
-            "moe_combine", "moe_forward")
+            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward")
 
 _lib = None
 
@@ -85,6 +85,10 @@ def lib():
         "moe_permute": [cfgp, I64, P, ctypes.POINTER(moe_routing), P],
         "moe_expert_ffn": [cfgp, I64, P, ctypes.POINTER(moe_routing), ctypes.POINTER(moe_weights),
                            P, P, P, P, P],
+        "moe_expert_up": [cfgp, I64, P, ctypes.POINTER(moe_routing), ctypes.POINTER(moe_weights),
+                          P, P, P],
+        "moe_expert_down": [cfgp, I64, ctypes.POINTER(moe_routing), ctypes.POINTER(moe_weights),
+                            P, P, P, P, P],
         "moe_combine": [cfgp, I64, P, P, P, ctypes.POINTER(moe_routing), P, P, P],
         "moe_forward": [cfgp, I64, P, ctypes.POINTER(moe_weights), P, P, P, P, SZ, P],
     }
@@ -204,6 +208,19 @@ def moe_expert_ffn(cfg: moe_config, T: int, x, routing: Routing, weights: moe_we
     _check(lib().moe_expert_ffn(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(routing.struct),
                                 ctypes.byref(weights), _ptr(h), _ptr(y_pairs), _ptr(hs), _ptr(z),
                                 _stream(stream)))
+
+
+def moe_expert_up(cfg: moe_config, T: int, x, routing: Routing, weights: moe_weights, h, hs=None,
+                  stream=None) -> None:
+    _check(lib().moe_expert_up(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(routing.struct),
+                               ctypes.byref(weights), _ptr(h), _ptr(hs), _stream(stream)))
+
+
+def moe_expert_down(cfg: moe_config, T: int, routing: Routing, weights: moe_weights, h, hs, y_pairs,
+                    z=None, stream=None) -> None:
+    _check(lib().moe_expert_down(ctypes.byref(cfg), T, ctypes.byref(routing.struct),
+                                 ctypes.byref(weights), _ptr(h), _ptr(hs), _ptr(y_pairs), _ptr(z),
+                                 _stream(stream)))
 
 
 def moe_combine(cfg: moe_config, T: int, u, z, y_pairs, routing: Routing, topk_w, out,

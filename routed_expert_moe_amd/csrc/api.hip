@@ -218,12 +218,14 @@ moe_status do_gate(const moe_config &c, int64_t T, const void *x, const void *w_
   return ok();
 }
 
+// which: 1 = gate/up half, 2 = down half, 3 = both
 moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routing &r,
-                  const moe_weights &w, void *h, void *y, void *hs, void *z, hipStream_t st) {
+                  const moe_weights &w, void *h, void *y, void *hs, void *z, hipStream_t st,
+                  int which = 3) {
   const Plan p = plan_for(c, T);
   const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim;
   const bool fp8 = c.weight_dtype == MOE_FP8_E4M3_B128;
-  const bool shared = z != nullptr && c.n_shared > 0;
+  const bool shared = hs != nullptr && (which == 1 || z != nullptr) && c.n_shared > 0;
   const int32_t dense_tiles = static_cast<int32_t>((T + p.tile_m - 1) / p.tile_m);
 
   Segment up[2] = {}, dn[2] = {};
@@ -284,21 +286,16 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
     dn[1].ldc = D;
     dn[1].n_tiles_host = dense_tiles;
   }
-  hipError_t e;
-  switch (p.path) {
-    case PATH_F32:
-      e = launch_gemm_f32(up, nseg, p.tile_m, EPI_SWIGLU, st);
-      if (e == hipSuccess) e = launch_gemm_f32(dn, nseg, p.tile_m, EPI_STORE, st);
-      break;
-    case PATH_MFMA:
-      e = launch_gemm_mfma(up, nseg, p.tile_m, EPI_SWIGLU, false, st);
-      if (e == hipSuccess) e = launch_gemm_mfma(dn, nseg, p.tile_m, EPI_STORE, false, st);
-      break;
-    default:
-      e = launch_gemm_skinny(up, nseg, EPI_SWIGLU, fp8, false, st);
-      if (e == hipSuccess) e = launch_gemm_skinny(dn, nseg, EPI_STORE, fp8, false, st);
-      break;
-  }
+  auto run = [&](Segment *segs, Epilogue epi) -> hipError_t {
+    switch (p.path) {
+      case PATH_F32: return launch_gemm_f32(segs, nseg, p.tile_m, epi, st);
+      case PATH_MFMA: return launch_gemm_mfma(segs, nseg, p.tile_m, epi, false, st);
+      default: return launch_gemm_skinny(segs, nseg, epi, fp8, false, st);
+    }
+  };
+  hipError_t e = hipSuccess;
+  if (which & 1) e = run(up, EPI_SWIGLU);
+  if (e == hipSuccess && (which & 2)) e = run(dn, EPI_STORE);
   if (e != hipSuccess) return device_fail(e, "expert FFN launch");
   return ok();
 }
@@ -428,6 +425,37 @@ moe_status moe_expert_ffn(const moe_config *cfg, int64_t T, const void *x,
   }
   if (T == 0) return ok();
   return do_ffn(*cfg, T, x, *r, *w, h, y_pairs, hs, z, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_up(const moe_config *cfg, int64_t T, const void *x, const moe_routing *r,
+                         const moe_weights *w, void *h, void *hs, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_NEED(x, "x");
+  MOE_TRY(check_routing(*cfg, T, r));
+  MOE_TRY(check_weights(*cfg, w, hs != nullptr));
+  MOE_NEED(h, "h");
+  MOE_OPT(hs, "hs");
+  if (T == 0) return ok();
+  return do_ffn(*cfg, T, x, *r, *w, h, nullptr, hs, nullptr, static_cast<hipStream_t>(stream), 1);
+}
+
+moe_status moe_expert_down(const moe_config *cfg, int64_t T, const moe_routing *r,
+                           const moe_weights *w, const void *h, const void *hs, void *y_pairs,
+                           void *z, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_routing(*cfg, T, r));
+  MOE_TRY(check_weights(*cfg, w, z != nullptr));
+  MOE_NEED(h, "h");
+  MOE_NEED(y_pairs, "y_pairs");
+  if (z != nullptr && cfg->n_shared > 0) {
+    MOE_NEED(hs, "hs");
+    MOE_NEED(z, "z");
+  }
+  if (T == 0) return ok();
+  return do_ffn(*cfg, T, nullptr, *r, *w, const_cast<void *>(h), y_pairs, const_cast<void *>(hs),
+                z, static_cast<hipStream_t>(stream), 2);
 }
 
 moe_status moe_combine(const moe_config *cfg, int64_t T, const void *u, const void *z,
