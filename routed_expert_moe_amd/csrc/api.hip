@@ -207,7 +207,8 @@ moe_status do_gate(const moe_config &c, int64_t T, const void *x, const void *w_
     e = launch_gemm_f32(&s, 1, kF32TileM, EPI_STORE, st);
   } else if (T >= 64) {
     s.n_tiles_host = static_cast<int32_t>((T + kMfmaTileM - 1) / kMfmaTileM);
-    e = launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
+    e = gemm_mfma2_supported(&s, 1) ? launch_gemm_mfma2(&s, 1, EPI_STORE, true, st)
+                                    : launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
   } else {
     s.n_tiles_host = static_cast<int32_t>((T + kSkinnyTileM - 1) / kSkinnyTileM);
     e = launch_gemm_skinny(&s, 1, EPI_STORE, false, true, st);
@@ -289,7 +290,9 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
   auto run = [&](Segment *segs, Epilogue epi) -> hipError_t {
     switch (p.path) {
       case PATH_F32: return launch_gemm_f32(segs, nseg, p.tile_m, epi, st);
-      case PATH_MFMA: return launch_gemm_mfma(segs, nseg, p.tile_m, epi, false, st);
+      case PATH_MFMA:
+        if (gemm_mfma2_supported(segs, nseg)) return launch_gemm_mfma2(segs, nseg, epi, false, st);
+        return launch_gemm_mfma(segs, nseg, p.tile_m, epi, false, st);
       default: return launch_gemm_skinny(segs, nseg, epi, fp8, false, st);
     }
   };

@@ -82,6 +82,9 @@ hipError_t launch_gemm_f32(const Segment *segs, int nseg, int tile_m, Epilogue e
                            hipStream_t st);
 hipError_t launch_gemm_mfma(const Segment *segs, int nseg, int tile_m, Epilogue epi,
                             bool out_f32, hipStream_t st);
+bool gemm_mfma2_supported(const Segment *segs, int nseg);
+hipError_t launch_gemm_mfma2(const Segment *segs, int nseg, Epilogue epi, bool out_f32,
+                             hipStream_t st);
 hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool w_fp8,
                               bool out_f32, hipStream_t st);
 

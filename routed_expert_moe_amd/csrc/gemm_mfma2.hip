@@ -1,0 +1,330 @@
+// Grouped GEMM on bf16 MFMA for prefill-sized tiles:
+//     C[rows, n] = A[rows, k] * B_e[n, k]^T,  fp32 accumulation.
+//
+// Workgroup tile 128 (rows of A) x 512 (rows of B) x 64 (K); four wavefronts
+// side by side, each owning all 128 rows and its own 128 rows of B, as 4 x 4
+// blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).  A
+// 128 x 128 wavefront tile halves the LDS bytes read per MFMA compared with a
+// 64 x 128 one, which is what bounds smaller tiles on this chip.
+//
+// Operands go from global memory straight into LDS with
+// global_load_lds_dwordx4 (two 80 KiB stages; the loads of step k+1 are spread
+// over the four K slices of step k).  Each 1 KiB wave load fills eight
+// 128-byte LDS rows; the lane that writes physical chunk p of row r fetches
+// logical chunk p ^ ((r >> 1) & 7).  An operand read serves 16 lanes at a time,
+// 16 consecutive rows at one logical chunk: two rows share each 256-byte bank
+// line, and the swizzle sends the 8 rows of each parity to 8 different chunks,
+// so the 16 reads cover all 64 banks once.
+//
+// The MFMA takes the weight fragment as its first operand, so each lane ends
+// with four consecutive output columns of one row: one 16-byte store for fp32
+// output, one 8-byte LDS store for bf16 output, which is then written to
+// memory in whole-row 1 KiB runs per wavefront.
+//
+// The grid is persistent: one workgroup per CU, the work list (routed tiles x
+// column blocks, then the dense segment's) cut into eight contiguous ranges,
+// one per XCD (workgroup b runs on XCD b % 8), so tiles sharing gathered A
+// rows or an expert's weights meet in the same L2.
+//
+// Requires K % 64 == 0.  Rows outside the valid range are clamped to a valid
+// row; their results are never stored (dense) or never read (routed padding).
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 128, BN = 512, BK = 64;
+#ifndef MOE_MFMA2_WAVES
+#define MOE_MFMA2_WAVES 8
+#endif
+constexpr int kWaves = MOE_MFMA2_WAVES;                 // wavefronts per workgroup, side by side
+constexpr int kThreads = 64 * kWaves;
+constexpr int NJ = BN / kWaves / 32;                    // 32-row B sub-tiles per wavefront
+constexpr int kStages = 2;
+constexpr int kRowBytes = BK * 2;                       // 128 B per LDS row
+constexpr int kATileBytes = BM * kRowBytes;             // 16 KiB
+constexpr int kBTileBytes = BN * kRowBytes;             // 64 KiB
+constexpr int kStageBytes = kATileBytes + kBTileBytes;  // 80 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;        // 160 KiB
+constexpr int kXcds = 8;
+constexpr int kALoads = BM * kRowBytes / 1024 / kWaves;  // wave loads of A per wavefront
+constexpr int kBLoads = BN * kRowBytes / 1024 / kWaves;  // wave loads of B per wavefront
+constexpr int kLoads = kALoads + kBLoads;                // per wavefront per K step
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+struct Work2 {
+  Segment seg[2];
+  int nseg;
+  int nblk_n[2];
+};
+
+__device__ __forceinline__ void load_lds16(const void *g, char *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t *)(g), (lds_void_t *)(lds_wave_base), 16, 0, 0);
+}
+
+// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+template <int EPI, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int lrow = lane >> 3, pch = lane & 7;    // DMA: row within the 8-row wave load, chunk
+
+  // ---- work list: segment 0 tiles x column blocks, then segment 1
+  const int tiles0 = uniform(wk.seg[0].n_tiles_dev ? *wk.seg[0].n_tiles_dev : wk.seg[0].n_tiles_host);
+  const int items0 = tiles0 * wk.nblk_n[0];
+  const int items1 = wk.nseg > 1 ? wk.seg[1].n_tiles_host * wk.nblk_n[1] : 0;
+  const int total = items0 + items1;
+  const int nloc = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int w_end = min(total, (xcd + 1) * chunk);
+
+  for (int w = xcd * chunk + loc; w < w_end; w += nloc) {
+    const int si = w < items0 ? 0 : 1;
+    const Segment &sg = wk.seg[si];
+    const int local = si == 0 ? w : w - items0;
+    const int tile = local / wk.nblk_n[si];
+    const int nb = local - tile * wk.nblk_n[si];
+    const bool dense = sg.n_tiles_dev == nullptr;
+    const int row0 = uniform(dense ? tile * BM : sg.tile_row[tile]);
+    const int expert = uniform(dense ? 0 : sg.tile_expert[tile]);
+    const int K = sg.k;
+    const int nk = K / BK;
+    const int half_n = sg.n / 2;
+
+    // ---- global sources of this lane's DMA rows
+    const uint16_t *A = static_cast<const uint16_t *>(sg.a);
+    const uint16_t *asrc[kALoads];
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) {
+      const int r = (wave * kALoads + i) * 8 + lrow;    // A tile row
+      const int grow = row0 + r;
+      int64_t arow;
+      if (sg.gather != nullptr) {
+        const int pair = sg.gather[grow];
+        arow = pair >= 0 ? pair / sg.topk : 0;
+      } else {
+        arow = (!dense || grow < sg.a_rows) ? grow : sg.a_rows - 1;
+      }
+      asrc[i] = A + arow * sg.lda + (pch ^ swz(r)) * 8;
+    }
+    const uint16_t *Bm = static_cast<const uint16_t *>(sg.b) + static_cast<int64_t>(expert) * sg.b_stride;
+    auto bptr = [&](int i) -> const uint16_t * {
+      const int r = (wave * kBLoads + i) * 8 + lrow;    // B tile row
+      int brow;
+      if (EPI == EPI_SWIGLU) {
+        const int col = nb * (BN / 2) + (r & (BN / 2 - 1));
+        const int c = col < half_n ? col : half_n - 1;
+        brow = r < BN / 2 ? c : half_n + c;
+      } else {
+        brow = nb * BN + r;
+        if (brow >= sg.n) brow = sg.n - 1;
+      }
+      return Bm + static_cast<int64_t>(brow) * K + (pch ^ swz(r)) * 8;
+    };
+    auto issue_one = [&](int li, int kt) {
+      char *st = lds + (kt & 1) * kStageBytes;
+      const int k0 = kt * BK;
+      if (li < kALoads)
+        load_lds16(asrc[li] + k0, st + (wave * kALoads + li) * 1024);
+      else
+        load_lds16(bptr(li - kALoads) + k0, st + kATileBytes + (wave * kBLoads + li - kALoads) * 1024);
+    };
+
+    f32x16_t acc[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // LDS rows read by this lane: A rows i*32 + l32; B rows of sub-tile j
+    // SwiGLU: sub-tiles [0, NJ/2) are gate rows, [NJ/2, NJ) the matching up rows
+    int brow_l[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      brow_l[j] = (EPI == EPI_SWIGLU ? (j / (NJ / 2)) * (BN / 2) + wave * (NJ / 2) * 32 + (j % (NJ / 2)) * 32
+                                     : wave * NJ * 32 + j * 32) + l32;
+
+    auto read_frags = [&](const char *st, int s, bf16x8_t (&af)[4], bf16x8_t (&bf)[NJ]) {
+      const u32x4_t *As = reinterpret_cast<const u32x4_t *>(st);
+      const u32x4_t *Bs = reinterpret_cast<const u32x4_t *>(st + kATileBytes);
+      const int c = 2 * s + khalf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + l32;
+        af[i] = __builtin_bit_cast(bf16x8_t, As[r * 8 + (c ^ swz(r))]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = brow_l[j];
+        bf[j] = __builtin_bit_cast(bf16x8_t, Bs[r * 8 + (c ^ swz(r))]);
+      }
+    };
+
+#pragma unroll
+    for (int li = 0; li < kLoads; ++li) issue_one(li, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt: this wave's loads are the only ones in flight; then a bare barrier
+      // (__syncthreads would add a release fence that drains nothing useful here)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+      const char *st = lds + (kt & 1) * kStageBytes;
+      const bool more = kt + 1 < nk;
+      bf16x8_t af[2][4], bf[2][NJ];
+      read_frags(st, 0, af[0], bf[0]);
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        if (more) {   // a quarter of the loads of step kt+1 (the other stage is free)
+#pragma unroll
+          for (int q = s * kLoads / 4; q < (s + 1) * kLoads / 4; ++q) issue_one(q, kt + 1);
+        }
+        if (s + 1 < BK / 16) read_frags(st, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)   // weight fragment first: lanes end with 4 consecutive columns
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s & 1][j], af[s & 1][i], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // all waves done with both stages before the next item refills them
+
+    // ---- epilogue.  acc[i][j][4g + t] is C[row i*32 + l32][col j*32 + 8g + 4*khalf + t].
+    // bf16 results go through LDS (both stages are free now): each lane writes its
+    // 4 consecutive columns as one 8-byte LDS store, then every wavefront writes
+    // 1 KiB runs of whole output rows (eight full 128-byte lines per store).
+    if (OUT_F32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int grow = row0 + i * 32 + l32;
+        if (dense && grow >= sg.a_rows) continue;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = nb * BN + wave * NJ * 32 + j * 32 + 8 * g + 4 * khalf;
+            if (col >= sg.n) continue;
+            const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            *reinterpret_cast<f32x4_t *>(static_cast<float *>(sg.c) + static_cast<int64_t>(grow) * sg.ldc + col) = v;
+          }
+      }
+    } else {
+      constexpr int OUTC = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns of the tile
+      constexpr int LDR = OUTC * 2 + 16;                       // padded LDS row, bytes
+      char *ot = lds;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lr = i * 32 + l32;
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int jj = 0; jj < NJ / 2; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int lc = wave * (NJ / 2) * 32 + jj * 32 + 8 * g + 4 * khalf;
+              float h[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) h[t] = silu_mul(acc[i][jj][4 * g + t], acc[i][jj + NJ / 2][4 * g + t]);
+              uint2 v;
+              v.x = pack_bf16x2(h[0], h[1]);
+              v.y = pack_bf16x2(h[2], h[3]);
+              *reinterpret_cast<uint2 *>(ot + lr * LDR + lc * 2) = v;
+              __builtin_amdgcn_sched_barrier(0);   // keep accumulator reads next to their store
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int lc = wave * NJ * 32 + j * 32 + 8 * g + 4 * khalf;
+              uint2 v;
+              v.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+              v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+              *reinterpret_cast<uint2 *>(ot + lr * LDR + lc * 2) = v;
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+      }
+      __syncthreads();
+      constexpr int CPR = OUTC / 8;                  // 16-byte chunks per row
+      const int ncols = EPI == EPI_SWIGLU ? half_n : sg.n;
+      const int col0 = nb * OUTC;
+      for (int cidx = threadIdx.x; cidx < BM * CPR; cidx += kThreads) {
+        const int lr = cidx / CPR, cc = cidx - lr * CPR;
+        const int grow = row0 + lr, gcol = col0 + cc * 8;
+        if ((dense && grow >= sg.a_rows) || gcol >= ncols) continue;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ot + lr * LDR + cc * 16);
+        *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(sg.c) + static_cast<int64_t>(grow) * sg.ldc + gcol) = v;
+      }
+      __syncthreads();   // the next item's loads refill this LDS
+    }
+    // gfx9 counts stores in vmcnt: drain them so the next item's waits count only its loads
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  }
+}
+
+template <int EPI, bool OUT_F32>
+hipError_t launch_one(const Work2 &wk, int grid, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_mfma2_kernel<EPI, OUT_F32>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_mfma2_kernel<EPI, OUT_F32>), dim3(grid), dim3(kThreads), kLdsBytes, st, wk);
+  return hipGetLastError();
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+}  // namespace
+
+bool gemm_mfma2_supported(const Segment *segs, int nseg) {
+  for (int s = 0; s < nseg; ++s)
+    if (segs[s].k % BK != 0 || segs[s].k <= 0 || segs[s].n % 8 != 0 || segs[s].ldc % 8 != 0) return false;
+  return true;
+}
+
+hipError_t launch_gemm_mfma2(const Segment *segs, int nseg, Epilogue epi, bool out_f32,
+                             hipStream_t st) {
+  Work2 wk{};
+  wk.nseg = nseg;
+  int64_t cap = 0;
+  for (int s = 0; s < nseg; ++s) {
+    wk.seg[s] = segs[s];
+    const int ncols = epi == EPI_SWIGLU ? segs[s].n / 2 : segs[s].n;
+    const int per = epi == EPI_SWIGLU ? BN / 2 : BN;
+    wk.nblk_n[s] = (ncols + per - 1) / per;
+    cap += static_cast<int64_t>(segs[s].n_tiles_host) * wk.nblk_n[s];
+  }
+  if (cap == 0) return hipSuccess;
+  if (cap >= (1ll << 31)) return hipErrorInvalidValue;
+  int grid = cu_count() / kXcds * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  if (epi == EPI_SWIGLU) return launch_one<EPI_SWIGLU, false>(wk, grid, st);
+  if (out_f32) return launch_one<EPI_STORE, true>(wk, grid, st);
+  return launch_one<EPI_STORE, false>(wk, grid, st);
+}
+
+}  // namespace moe
