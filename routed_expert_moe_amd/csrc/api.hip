@@ -210,8 +210,7 @@ moe_status do_gate(const moe_config &c, int64_t T, const void *x, const void *w_
     e = gemm_mfma2_supported(&s, 1) ? launch_gemm_mfma2(&s, 1, EPI_STORE, true, st)
                                     : launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
   } else {
-    s.n_tiles_host = static_cast<int32_t>((T + kSkinnyTileM - 1) / kSkinnyTileM);
-    e = launch_gemm_skinny(&s, 1, EPI_STORE, false, true, st);
+    e = launch_gate_logits_gemv(c, T, x, w_gate, logits, st);
   }
   if (e != hipSuccess) return device_fail(e, "gate logits launch");
   e = launch_gate_route(c, T, logits, bias, idx, w, keys, st);

@@ -1,6 +1,6 @@
 // Combine (DeepSeek-V3 notes page, "DeepSeekMoE" total-output equation):
 //   out[t] = u[t] + z[t] + sum_k w[t,k] * y[pair_row[t*K+k]]
-// One workgroup per token; every thread owns 16-byte column chunks and sums in
+// grid.x is the token, grid.y splits the row; every thread owns 16-byte column chunks and sums in
 // fp32 in a fixed order (u, z, then slots k = 0..K-1, which the gate emits in
 // ascending expert order), rounding once.  No atomics: the result is unique.
 #include "common.hpp"
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int
   __syncthreads();
   constexpr int V = BF16 ? 8 : 4;   // elements per 16-byte chunk
   const int nchunks = D / V;
-  for (int c = threadIdx.x; c < nchunks; c += kThreads) {
+  for (int c = blockIdx.y * kThreads + threadIdx.x; c < nchunks; c += kThreads * gridDim.y) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.0f;
@@ -73,7 +73,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int
 hipError_t launch_combine(const moe_config &cfg, int64_t T, const void *u, const void *z,
                           const void *y, const moe_routing &r, const float *w, void *out,
                           hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(T)), block(kThreads);
+  // grid.x = token; grid.y spreads a row's 16-byte chunks over workgroups so a
+  // short batch still occupies many CUs
+  const int V = cfg.act_dtype == MOE_BF16 ? 8 : 4;
+  const int nchunks = cfg.dim / V;
+  const int per_token = T >= 1024 ? 1 : (nchunks + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(per_token)), block(kThreads);
   if (cfg.act_dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, st, T, cfg.dim, cfg.top_k, u, z, y,
                        r.pair_row, w, out, cfg.add_residual);

@@ -71,6 +71,8 @@ struct Plan {
 hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logits,
                              const float *bias, int32_t *topk_idx, float *topk_w, float *keys,
                              hipStream_t st);
+hipError_t launch_gate_logits_gemv(const moe_config &cfg, int64_t T, const void *x,
+                                   const void *w_gate, float *logits, hipStream_t st);
 hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_idx,
                           const moe_routing &r, hipStream_t st);
 hipError_t launch_combine(const moe_config &cfg, int64_t T, const void *u, const void *z,

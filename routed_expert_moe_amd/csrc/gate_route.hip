@@ -193,3 +193,71 @@ hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logi
 }
 
 }  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Gate logits for small batches (T < 64, bf16): l[t][e] = x_t . W_g[e].
+// A GEMM tile would leave most CUs idle here, so one wavefront per expert row
+// streams W_g once (E wavefronts in parallel) and forms the dot products of up
+// to 8 tokens per pass in fp32, lanes striding over K in 16-byte pieces, then
+// a butterfly reduction across the wavefront.
+namespace moe {
+namespace {
+
+constexpr int kGemvTokens = 8;
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4_t v, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void gate_logits_gemv_kernel(const uint16_t *__restrict__ x,
+                                                               const uint16_t *__restrict__ wg,
+                                                               int T, int E, int K,
+                                                               float *__restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;   // uniform per wavefront
+  const uint16_t *wrow = wg + static_cast<int64_t>(e) * K;
+  for (int t0 = 0; t0 < T; t0 += kGemvTokens) {
+    const int nt = min(kGemvTokens, T - t0);
+    float acc[kGemvTokens];
+#pragma unroll
+    for (int t = 0; t < kGemvTokens; ++t) acc[t] = 0.0f;
+#pragma unroll 2
+    for (int k = lane * 8; k < K; k += 64 * 8) {
+      float w[8];
+      bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(wrow + k), w);
+#pragma unroll
+      for (int t = 0; t < kGemvTokens; ++t) {
+        if (t < nt) {
+          float xv[8];
+          bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(x + static_cast<int64_t>(t0 + t) * K + k), xv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[t] = fmaf(w[i], xv[i], acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kGemvTokens; ++t) {
+      float v = acc[t];
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0 && t < nt) logits[static_cast<int64_t>(t0 + t) * E + e] = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate_logits_gemv(const moe_config &cfg, int64_t T, const void *x,
+                                   const void *w_gate, float *logits, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((cfg.n_routed + 3) / 4)), block(256);
+  hipLaunchKernelGGL(gate_logits_gemv_kernel, grid, block, 0, st, static_cast<const uint16_t *>(x),
+                     static_cast<const uint16_t *>(w_gate), static_cast<int>(T), cfg.n_routed, cfg.dim,
+                     logits);
+  return hipGetLastError();
+}
+
+}  // namespace moe
