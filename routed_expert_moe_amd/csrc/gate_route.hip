@@ -196,14 +196,17 @@ hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logi
 
 // ---------------------------------------------------------------------------
 // Gate logits for small batches (T < 64, bf16): l[t][e] = x_t . W_g[e].
-// A GEMM tile would leave most CUs idle here, so one wavefront per expert row
-// streams W_g once (E wavefronts in parallel) and forms the dot products of up
-// to 8 tokens per pass in fp32, lanes striding over K in 16-byte pieces, then
-// a butterfly reduction across the wavefront.
+// A GEMM tile would leave most CUs idle here.  Each workgroup takes 4 expert
+// rows; its 8 wavefronts split K eight ways and form the dot products of up to
+// 8 tokens per pass in fp32 (lanes stride over their K range in 16-byte
+// pieces), reduce across lanes with a butterfly, then across wavefronts in LDS
+// in a fixed order.
 namespace moe {
 namespace {
 
 constexpr int kGemvTokens = 8;
+constexpr int kGemvExperts = 4;
+constexpr int kGemvWaves = 8;
 
 __device__ __forceinline__ void bf16x8_to_f32(const u32x4_t v, float (&f)[8]) {
 #pragma unroll
@@ -213,39 +216,57 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4_t v, float (&f)[8]) {
   }
 }
 
-__global__ __launch_bounds__(256) void gate_logits_gemv_kernel(const uint16_t *__restrict__ x,
-                                                               const uint16_t *__restrict__ wg,
-                                                               int T, int E, int K,
-                                                               float *__restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;   // uniform per wavefront
-  const uint16_t *wrow = wg + static_cast<int64_t>(e) * K;
+__global__ __launch_bounds__(64 * kGemvWaves) void gate_logits_gemv_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg, int T, int E, int K,
+    float *__restrict__ logits) {
+  __shared__ float part[kGemvWaves][kGemvExperts * kGemvTokens];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e0 = blockIdx.x * kGemvExperts;
+  const int units = K / 8;                                    // 16-byte pieces per row
+  const int u0 = wave * units / kGemvWaves, u1 = (wave + 1) * units / kGemvWaves;
   for (int t0 = 0; t0 < T; t0 += kGemvTokens) {
     const int nt = min(kGemvTokens, T - t0);
-    float acc[kGemvTokens];
+    float acc[kGemvExperts][kGemvTokens];
 #pragma unroll
-    for (int t = 0; t < kGemvTokens; ++t) acc[t] = 0.0f;
-#pragma unroll 2
-    for (int k = lane * 8; k < K; k += 64 * 8) {
-      float w[8];
-      bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(wrow + k), w);
+    for (int j = 0; j < kGemvExperts; ++j)
+#pragma unroll
+      for (int t = 0; t < kGemvTokens; ++t) acc[j][t] = 0.0f;
+    for (int u = u0 + lane; u < u1; u += 64) {
+      const int k = u * 8;
+      float w[kGemvExperts][8];
+#pragma unroll
+      for (int j = 0; j < kGemvExperts; ++j) {
+        if (e0 + j < E) bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(wg + static_cast<int64_t>(e0 + j) * K + k), w[j]);
+        else for (int i = 0; i < 8; ++i) w[j][i] = 0.0f;
+      }
 #pragma unroll
       for (int t = 0; t < kGemvTokens; ++t) {
         if (t < nt) {
           float xv[8];
           bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(x + static_cast<int64_t>(t0 + t) * K + k), xv);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[t] = fmaf(w[i], xv[i], acc[t]);
+          for (int j = 0; j < kGemvExperts; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][t] = fmaf(w[j][i], xv[i], acc[j][t]);
         }
       }
     }
 #pragma unroll
-    for (int t = 0; t < kGemvTokens; ++t) {
-      float v = acc[t];
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0 && t < nt) logits[static_cast<int64_t>(t0 + t) * E + e] = v;
+    for (int j = 0; j < kGemvExperts; ++j)
+#pragma unroll
+      for (int t = 0; t < kGemvTokens; ++t) {
+        float v = acc[j][t];
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0) part[wave][j * kGemvTokens + t] = v;
+      }
+    __syncthreads();
+    if (threadIdx.x < kGemvExperts * kGemvTokens) {
+      const int j = threadIdx.x / kGemvTokens, t = threadIdx.x % kGemvTokens;
+      float v = 0.0f;
+      for (int w = 0; w < kGemvWaves; ++w) v += part[w][threadIdx.x];   // K order
+      if (t < nt && e0 + j < E) logits[static_cast<int64_t>(t0 + t) * E + e0 + j] = v;
     }
+    __syncthreads();
   }
 }
 
@@ -253,7 +274,8 @@ __global__ __launch_bounds__(256) void gate_logits_gemv_kernel(const uint16_t *_
 
 hipError_t launch_gate_logits_gemv(const moe_config &cfg, int64_t T, const void *x,
                                    const void *w_gate, float *logits, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((cfg.n_routed + 3) / 4)), block(256);
+  const dim3 grid(static_cast<unsigned>((cfg.n_routed + kGemvExperts - 1) / kGemvExperts));
+  const dim3 block(64 * kGemvWaves);
   hipLaunchKernelGGL(gate_logits_gemv_kernel, grid, block, 0, st, static_cast<const uint16_t *>(x),
                      static_cast<const uint16_t *>(w_gate), static_cast<int>(T), cfg.n_routed, cfg.dim,
                      logits);

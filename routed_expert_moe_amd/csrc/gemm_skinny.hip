@@ -3,12 +3,13 @@
 //
 // At decode the weights are nearly all of the bytes, so the kernel is built to
 // keep HBM busy:
-//  * persistent grid (four workgroups per CU); every wavefront takes work
+//  * persistent grid (as many workgroups as fit on the CUs at once); every wavefront takes work
 //    items (tile, pair of 16-row weight groups) from one list that holds only
 //    the tiles in use, so no workgroup is launched for an untouched expert;
 //  * each wavefront streams its two groups over the whole K, loading 128-wide
-//    K block k+1 while it multiplies block k (16 wavefronts per CU keep about
-//    64 KiB of weights in flight per CU, enough to cover HBM latency);
+//    K blocks k+1 and k+2 while it multiplies block k (with 12-16 wavefronts
+//    per CU about 100 KiB of weights stay in flight per CU, which covers the
+//    several-microsecond HBM latency under full load);
 //  * within a 128-wide K block, lane (row n = lane%16, quarter q = lane/16)
 //    owns K positions [32q, 32q+32) of its weight row, so it reads whole
 //    16-byte pieces; the A fragments use the same K permutation, which a dot
@@ -27,8 +28,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBlocksPerCu = 4;
-constexpr int kChunk = 1;                 // 128-wide K blocks per pipeline step
 
 struct Work {
   Segment seg[2];
@@ -176,21 +175,19 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
       }
     };
 
-    // two chunk buffers: chunk c+1 loads while chunk c multiplies
-    KBlock<FP8> buf[2][kChunk];
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) load_kb(u, buf[0][u]);
-    const int nchunks = (kblocks + kChunk - 1) / kChunk;
-    for (int c = 0; c < nchunks; c += 2) {
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) load_kb((c + 1) * kChunk + u, buf[1][u]);
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) compute_kb(c * kChunk + u, buf[0][u]);
-      if (c + 1 >= nchunks) break;
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) load_kb((c + 2) * kChunk + u, buf[0][u]);
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) compute_kb((c + 1) * kChunk + u, buf[1][u]);
+    // three K-block buffers: blocks kb+1 and kb+2 load while kb multiplies
+    KBlock<FP8> buf[3];
+    load_kb(0, buf[0]);
+    load_kb(1, buf[1]);
+    for (int kb = 0; kb < kblocks; kb += 3) {
+      load_kb(kb + 2, buf[2]);
+      compute_kb(kb, buf[0]);
+      if (kb + 1 >= kblocks) break;
+      load_kb(kb + 3, buf[0]);
+      compute_kb(kb + 1, buf[1]);
+      if (kb + 2 >= kblocks) break;
+      load_kb(kb + 4, buf[1]);
+      compute_kb(kb + 2, buf[2]);
     }
 
     // epilogue: lane holds column l16 of the group (a weight row), tile rows 4q + r
@@ -245,10 +242,21 @@ hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool 
   if (cap == 0) return hipSuccess;
   if (cap >= (1ll << 31)) return hipErrorInvalidValue;
   int64_t blocks = (cap + kWaves - 1) / kWaves;
-  const int64_t max_blocks = static_cast<int64_t>(cu_count()) * kBlocksPerCu;
-  if (blocks > max_blocks) blocks = max_blocks;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-#define MOE_SKINNY(E_, F_, O_) hipLaunchKernelGGL((gemm_skinny_kernel<E_, F_, O_>), grid, block, 0, st, wk)
+  auto resident = [&](const void *fn) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    return static_cast<int64_t>(cu_count()) * per_cu;
+  };
+#define MOE_SKINNY(E_, F_, O_)                                                                  \
+  do {                                                                                          \
+    static int64_t max_blocks = 0;                                                              \
+    if (max_blocks == 0) max_blocks = resident(reinterpret_cast<const void *>(&gemm_skinny_kernel<E_, F_, O_>)); \
+    /* equal rounds: every wavefront gets the same number of items (no half-empty last round) */ \
+    const int64_t rounds = (blocks + max_blocks - 1) / max_blocks;                              \
+    const dim3 grid(static_cast<unsigned>((blocks + rounds - 1) / rounds)), block(kThreads);    \
+    hipLaunchKernelGGL((gemm_skinny_kernel<E_, F_, O_>), grid, block, 0, st, wk);                 \
+  } while (0)
   if (epi == EPI_SWIGLU) {
     if (w_fp8) MOE_SKINNY(EPI_SWIGLU, true, false);
     else MOE_SKINNY(EPI_SWIGLU, false, false);
