@@ -252,9 +252,7 @@ hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool 
   do {                                                                                          \
     static int64_t max_blocks = 0;                                                              \
     if (max_blocks == 0) max_blocks = resident(reinterpret_cast<const void *>(&gemm_skinny_kernel<E_, F_, O_>)); \
-    /* equal rounds: every wavefront gets the same number of items (no half-empty last round) */ \
-    const int64_t rounds = (blocks + max_blocks - 1) / max_blocks;                              \
-    const dim3 grid(static_cast<unsigned>((blocks + rounds - 1) / rounds)), block(kThreads);    \
+    const dim3 grid(static_cast<unsigned>(blocks < max_blocks ? blocks : max_blocks)), block(kThreads); \
     hipLaunchKernelGGL((gemm_skinny_kernel<E_, F_, O_>), grid, block, 0, st, wk);                 \
   } while (0)
   if (epi == EPI_SWIGLU) {
