@@ -11,9 +11,10 @@
 //    per CU about 100 KiB of weights stay in flight per CU, which covers the
 //    several-microsecond HBM latency under full load);
 //  * within a 128-wide K block, lane (row n = lane%16, quarter q = lane/16)
-//    owns K positions [32q, 32q+32) of its weight row, so it reads whole
-//    16-byte pieces; the A fragments use the same K permutation, which a dot
-//    product allows, and four MFMAs cover the block.
+//    owns 32 K positions of its weight row, chosen so that the four lanes of a
+//    row read one contiguous 64-byte run per load; the A fragments use the
+//    same K permutation, which a dot product allows, and four MFMAs cover the
+//    block.
 // fp8 weights (OCP e4m3fn, exact in bf16) are widened with v_cvt_pk_f32_fp8,
 // each 128-wide K block is accumulated separately and added times its fp32
 // block scale: acc += s[n/128][k/128] * partial.
@@ -117,28 +118,36 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
     const int64_t eoff = static_cast<int64_t>(expert) * sg.b_stride;
     const float *scale = FP8 ? sg.b_scale + static_cast<int64_t>(expert) * sg.s_stride : nullptr;
 
+    // K positions of this lane inside a 128-wide block, in MFMA order i = 0..3
+    // (8 each).  fp8: two 16-byte pieces at bytes 16q and 64 + 16q, so the four
+    // lanes of a row read one contiguous 64-byte run per load; bf16: four pieces
+    // at elements 32i/4 + 8q, i.e. bytes 64i + 16q, again contiguous per load.
+    auto kpos = [&](int kb, int i) -> int {
+      return FP8 ? kb * 128 + (i >> 1) * 64 + 16 * q + (i & 1) * 8 : kb * 128 + 32 * i + 8 * q;
+    };
     auto load_kb = [&](int kb, KBlock<FP8> &d) {
-      const int kq = kb * 128 + 32 * q;   // first K position of this lane's quarter
       const bool kin = kb < kblocks;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int k = kq + 8 * i;
+        const int k = kpos(kb, i);
         d.a[i] = (arow != nullptr && kin && k < K) ? *reinterpret_cast<const u32x4_t *>(arow + k)
                                                    : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         if (FP8) {
-          const uint8_t *wp = static_cast<const uint8_t *>(sg.b) + eoff + static_cast<int64_t>(wrow[g]) * K + kq;
+          const uint8_t *wp = static_cast<const uint8_t *>(sg.b) + eoff + static_cast<int64_t>(wrow[g]) * K;
           const bool ok = wvalid[g] && kin;
-          d.w[g][0] = ok ? *reinterpret_cast<const u32x4_t *>(wp) : u32x4_t{0, 0, 0, 0};
-          d.w[g][1] = ok ? *reinterpret_cast<const u32x4_t *>(wp + 16) : u32x4_t{0, 0, 0, 0};
+          d.w[g][0] = ok ? *reinterpret_cast<const u32x4_t *>(wp + kpos(kb, 0)) : u32x4_t{0, 0, 0, 0};
+          d.w[g][1] = ok ? *reinterpret_cast<const u32x4_t *>(wp + kpos(kb, 2)) : u32x4_t{0, 0, 0, 0};
         } else {
-          const uint16_t *wp = static_cast<const uint16_t *>(sg.b) + eoff + static_cast<int64_t>(wrow[g]) * K + kq;
+          const uint16_t *wp = static_cast<const uint16_t *>(sg.b) + eoff + static_cast<int64_t>(wrow[g]) * K;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            d.w[g][i] = (wvalid[g] && kin && kq + 8 * i < K) ? *reinterpret_cast<const u32x4_t *>(wp + 8 * i)
-                                                             : u32x4_t{0, 0, 0, 0};
+          for (int i = 0; i < 4; ++i) {
+            const int k = kpos(kb, i);
+            d.w[g][i] = (wvalid[g] && kin && k < K) ? *reinterpret_cast<const u32x4_t *>(wp + k)
+                                                    : u32x4_t{0, 0, 0, 0};
+          }
         }
       }
     };
