@@ -243,6 +243,7 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
   up[0].ldc = I;
   up[0].tile_row = r.tile_row;
   up[0].tile_expert = r.tile_expert;
+  up[0].expert_off = r.expert_off;
   up[0].n_tiles_dev = r.n_tiles;
   up[0].n_tiles_host = r.max_tiles;
 
@@ -258,6 +259,7 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
   dn[0].ldc = D;
   dn[0].tile_row = r.tile_row;
   dn[0].tile_expert = r.tile_expert;
+  dn[0].expert_off = r.expert_off;
   dn[0].n_tiles_dev = r.n_tiles;
   dn[0].n_tiles_host = r.max_tiles;
 

@@ -54,6 +54,7 @@ struct Segment {
   // segments cover rows [0, a_rows) in tiles of tile_m with expert 0.
   const int32_t *tile_row;
   const int32_t *tile_expert;
+  const int32_t *expert_off;   // first row of each expert, multiples of tile_m (routed only)
   const int32_t *n_tiles_dev;  // nullptr -> dense
   int32_t n_tiles_host;        // dense tile count, or capacity for routed
 };

@@ -23,8 +23,11 @@
 //
 // The grid is persistent: one workgroup per CU, the work list (routed tiles x
 // column blocks, then the dense segment's) cut into eight contiguous ranges,
-// one per XCD (workgroup b runs on XCD b % 8), so tiles sharing gathered A
-// rows or an expert's weights meet in the same L2.
+// one per XCD (workgroup b runs on XCD b % 8).  Inside each run of up to eight
+// M-tiles of one expert the list goes column block by column block, so the
+// tiles that read one block of an expert's weights start together on one XCD
+// and the block comes from HBM once; in tile-major order an expert's tiles
+// often landed in different rounds and each re-read the weights.
 //
 // Requires K % 64 == 0.  Rows outside the valid range are clamped to a valid
 // row; their results are never stored (dense) or never read (routed padding).
@@ -47,6 +50,7 @@ constexpr int kBTileBytes = BN * kRowBytes;             // 64 KiB
 constexpr int kStageBytes = kATileBytes + kBTileBytes;  // 80 KiB
 constexpr int kLdsBytes = kStages * kStageBytes;        // 160 KiB
 constexpr int kXcds = 8;
+constexpr int kGroup = 8;                               // M-tiles whose items interleave
 constexpr int kALoads = BM * kRowBytes / 1024 / kWaves;  // wave loads of A per wavefront
 constexpr int kBLoads = BN * kRowBytes / 1024 / kWaves;  // wave loads of B per wavefront
 constexpr int kLoads = kALoads + kBLoads;                // per wavefront per K step
@@ -87,16 +91,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
   const int total = items0 + items1;
   const int nloc = gridDim.x / kXcds;
   const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
-  const int chunk = (total + kXcds - 1) / kXcds;
+  const int chunk = ((total + kXcds - 1) / kXcds + 7) / 8 * 8;   // whole groups stay on one XCD more often
   const int w_end = min(total, (xcd + 1) * chunk);
 
   for (int w = xcd * chunk + loc; w < w_end; w += nloc) {
     const int si = w < items0 ? 0 : 1;
     const Segment &sg = wk.seg[si];
     const int local = si == 0 ? w : w - items0;
-    const int tile = local / wk.nblk_n[si];
-    const int nb = local - tile * wk.nblk_n[si];
     const bool dense = sg.n_tiles_dev == nullptr;
+    // Within a run of up to kGroup M-tiles of one expert (every tile of a dense
+    // segment shares one B), items go column block by column block, so the
+    // tiles reading the same block of B are adjacent in the list, run side by
+    // side on one XCD and fetch that block from HBM once.
+    int tile, nb;
+    {
+      const int nbk = wk.nblk_n[si];
+      const int slot = local / nbk;
+      int first, last;
+      if (dense) {
+        first = 0;
+        last = sg.n_tiles_host;
+      } else {
+        const int e = sg.tile_expert[slot];
+        first = sg.expert_off[e] / BM;
+        last = sg.expert_off[e + 1] / BM;
+      }
+      const int g0 = first + (slot - first) / kGroup * kGroup;
+      const int gs = min(kGroup, last - g0);
+      const int lg = local - g0 * nbk;
+      nb = uniform(lg / gs);
+      tile = uniform(g0 + lg - nb * gs);
+    }
     const int row0 = uniform(dense ? tile * BM : sg.tile_row[tile]);
     const int expert = uniform(dense ? 0 : sg.tile_expert[tile]);
     const int K = sg.k;
