@@ -14,7 +14,10 @@ roofline: the dominant kernel is the gate/up grouped GEMM (moe_expert_up);
 its duration comes from HIP events recorded around it on the stream it runs
 on, inside the timed region.  Its algorithmic work per launch is
 2*T*K*(2I)*D + 2*T*(2*S*I)*D flops and the bytes of the touched experts'
-W1/W3 (plus block scales), the shared W1/W3, x and the written h.
+W1/W3 (plus block scales), the shared W1/W3, x and the written h.  The bound
+reported is the ceiling that binds: with all 256 experts touched the prefill
+kernel's bytes take longer at 8 TB/s than its flops at 2.5 PFLOP/s, so it is
+HBM-bound on the roofline; both fractions are reported.
 """
 from __future__ import annotations
 
@@ -27,6 +30,60 @@ import time
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
+# Measured HBM traffic per launch of the two roofline kernels: rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the layer's
+# launches), scaled by what the same counters read for a 1 GiB device copy
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  The commands and per-dispatch values
+# are in profiles/.  Each figure is tied to a hash of its kernel's source and is
+# reported as null once that source has changed.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+COUNTERS = {
+    "prefill_up": {"sources": ("gemm_mfma2.hip", "common.hpp"),
+                   "sha256": "b292c827d020aad8d2692f218713c8f6a735b6e8c472cf185e27a2196add3ce8",
+                   "fetch_kib": 8671144, "write_kib": 362496,
+                   "profile": "profiles/gemm_mfma2_gate_up_v3_prefill_T8192_counters.md"},
+    "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
+                  "sha256": "3a9c66c4dbac940d8bbd188f9a574f101f7f5753765fe16a0ae3765b90789cfb",
+                  "fetch_kib": 849218, "write_kib": 4272,
+                  "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
+}
+
+
+def source_sha(names) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "routed_expert_moe_amd", "csrc")
+    for n in names:
+        with open(os.path.join(base, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from the counter runs, or None if the kernel changed since."""
+    c = COUNTERS[key]
+    if c["sha256"] is None or c["sha256"] != source_sha(c["sources"]):
+        return None
+    return (c["fetch_kib"] * FETCH_SCALE + c["write_kib"] * WRITE_SCALE) * 1024.0
+
+
+def roofline(flops: float, nbytes: float, ms: float, traffic, kernel: str) -> dict:
+    """The binding ceiling of a kernel: MFMA if its flops take longer at peak than its bytes, else HBM."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    tflops = flops / (ms / 1e3) / 1e12
+    gbs = nbytes / (ms / 1e3) / 1e9
+    r = {"kernel": kernel}
+    if t_mfma >= t_hbm:
+        r.update(bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                 frac=tflops / PEAK_BF16_TFLOPS)
+    else:
+        r.update(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s", frac=gbs / PEAK_HBM_GBS)
+    r.update(traffic=traffic, traffic_unit="bytes per launch (HBM, measured)",
+             avg_launch_ms=ms, algorithmic_flops=flops, algorithmic_bytes=nbytes,
+             mfma_frac=tflops / PEAK_BF16_TFLOPS, hbm_frac=gbs / PEAK_HBM_GBS)
+    return r
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -35,7 +92,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=0, help="default: 10x --steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -181,7 +238,6 @@ def main():
     fig = work_figures(layer, counts)
     ms = total_ms / args.steps
     tok_s = shape.T * args.steps / (total_ms / 1e3)
-    up_tflops = fig["flops_up"] / (up_ms / 1e3) / 1e12
     res = {
         "metric": "MoE-layer tokens/s + % MFMA peak (prefill), % HBM GB/s (decode), 1 MI355X",
         "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -195,11 +251,8 @@ def main():
                   "mfma_frac": fig["flops_layer"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                   "gbs": fig["bytes_layer"] / (ms / 1e3) / 1e9,
                   "hbm_frac": fig["bytes_layer"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
-        "roofline": {"kernel": "moe_expert_up (gate/up grouped GEMM + SwiGLU)", "bound": "mfma",
-                     "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": up_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "avg_launch_ms": up_ms, "algorithmic_flops": fig["flops_up"],
-                     "algorithmic_bytes": fig["bytes_up"]},
+        "roofline": roofline(fig["flops_up"], fig["bytes_up"], up_ms, measured_traffic("prefill_up"),
+                             "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)"),
         "wall_s": wall,
     }
     del p
@@ -213,17 +266,14 @@ def main():
     dtotal_ms, dup_ms, _ = time_pass(dp, dsteps, max(args.warmup, 3))
     dfig = work_figures(dlayer, dp.r.counts.cpu().numpy())
     dms = dtotal_ms / dsteps
-    up_gbs = dfig["bytes_up"] / (dup_ms / 1e3) / 1e9
     res["decode"] = {
         "workload": dshape.name, "T": dshape.T, "dtype": "fp8-e4m3 weights (128x128 fp32 scales), bf16 act",
         "steps": dsteps, "ms_per_step": dms, "tokens_per_s": dshape.T * dsteps / (dtotal_ms / 1e3),
         "experts_touched": dfig["touched"],
         "layer_gbs": dfig["bytes_layer"] / (dms / 1e3) / 1e9,
         "layer_hbm_frac": dfig["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
-        "roofline": {"kernel": "moe_expert_up (fp8 weight-streaming gate/up + SwiGLU)", "bound": "hbm",
-                     "achieved": up_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": up_gbs / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": dup_ms,
-                     "algorithmic_bytes": dfig["bytes_up"]},
+        "roofline": roofline(dfig["flops_up"], dfig["bytes_up"], dup_ms, measured_traffic("decode_up"),
+                             "moe_expert_up (fp8 weight-streaming gate/up + SwiGLU, gemm_skinny_kernel)"),
     }
     del dp, dlayer
     if not args.no_cpu_baseline:

@@ -10,6 +10,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxK = 32;
+constexpr int kBatch = 8;   // y rows loaded before the first is summed
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int K,
@@ -33,8 +34,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-    auto add_row = [&](const void *base, int64_t row, float scale, bool fma_mode) {
-      const u32x4_t v = reinterpret_cast<const u32x4_t *>(base)[(row * D) / V + c];
+    auto load = [&](const void *base, int64_t row) -> u32x4_t {
+      return reinterpret_cast<const u32x4_t *>(base)[(row * D) / V + c];
+    };
+    auto add_row = [&](const u32x4_t v, float scale, bool fma_mode) {
       if (BF16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -50,11 +53,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int
         }
       }
     };
-    if (residual) add_row(u, t, 1.0f, false);
-    if (z != nullptr) add_row(z, t, 1.0f, false);
-    for (int k = 0; k < K; ++k) {
-      const int row = s_row[k];
-      if (row >= 0) add_row(y, row, s_w[k], true);
+    // loads are issued in batches before their first use; an absent term (no
+    // residual, no shared expert, a dropped slot with row -1) reads row 0 of y,
+    // which always exists, and is skipped when summing
+    const u32x4_t vu = residual ? load(u, t) : load(y, 0);
+    const u32x4_t vz = z != nullptr ? load(z, t) : load(y, 0);
+    if (residual) add_row(vu, 1.0f, false);
+    if (z != nullptr) add_row(vz, 1.0f, false);
+    for (int k0 = 0; k0 < K; k0 += kBatch) {
+      u32x4_t v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = load(y, max(s_row[min(k0 + i, K - 1)], 0));
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (k0 + i < K && s_row[k0 + i] >= 0) add_row(v[i], s_w[k0 + i], true);
     }
     u32x4_t o;
     if (BF16) {

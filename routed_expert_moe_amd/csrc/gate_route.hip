@@ -22,22 +22,62 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+// Wavefront reductions without LDS traffic: DPP moves combine the 16 lanes of
+// each row (swap neighbours, swap pairs, mirror halves of 8, mirror 16), then
+// the four row results are read as scalars and combined in row order.  Every
+// lane gets the same value, and the order of operations is fixed.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return (static_cast<uint64_t>(dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
+         dpp_u32<CTRL>(static_cast<uint32_t>(v));
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(v)), l)));
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ float row_sum_f32(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
   return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 __device__ __forceinline__ float wave_sum_f32(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v = row_sum_f32(v);
+  return ((lane_f32(v, 0) + lane_f32(v, 16)) + lane_f32(v, 32)) + lane_f32(v, 48);
 }
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off);
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off);
-    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_u64(v, dpp_u64<kDppXor1>(v));
+  v = max_u64(v, dpp_u64<kDppXor2>(v));
+  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppMirror>(v));
+  return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 
 template <int NPL>
@@ -55,11 +95,14 @@ __global__ __launch_bounds__(256) void gate_route_kernel(
   if (t >= T) return;  // uniform per wavefront; no workgroup barrier below
 
   const float *lrow = logits + t * E;
-  float l[NPL], s[NPL], key[NPL];
+  // loads use clamped indices so they all issue before the first wait
+  float l[NPL], s[NPL], key[NPL], b[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane + 64 * j;
-    l[j] = e < E ? lrow[e] : -INFINITY;
+    const float v = lrow[min(e, E - 1)];
+    l[j] = e < E ? v : -INFINITY;
+    b[j] = bias != nullptr ? bias[min(e, E - 1)] : 0.0f;
   }
 
   // step 1: scores and ranked keys
@@ -68,7 +111,7 @@ __global__ __launch_bounds__(256) void gate_route_kernel(
     for (int j = 0; j < NPL; ++j) {
       const int e = lane + 64 * j;
       s[j] = 1.0f / (1.0f + expf(-l[j]));
-      key[j] = bias != nullptr && e < E ? s[j] + bias[e] : s[j];
+      key[j] = bias != nullptr && e < E ? s[j] + b[j] : s[j];
     }
   } else {
     float m = -INFINITY;
@@ -87,7 +130,7 @@ __global__ __launch_bounds__(256) void gate_route_kernel(
     for (int j = 0; j < NPL; ++j) {
       const int e = lane + 64 * j;
       s[j] = s[j] / sum;
-      key[j] = bias != nullptr && e < E ? s[j] + bias[e] : l[j];
+      key[j] = bias != nullptr && e < E ? s[j] + b[j] : l[j];
     }
   }
 #pragma unroll
@@ -110,6 +153,7 @@ __global__ __launch_bounds__(256) void gate_route_kernel(
     if (lane < G) {
       float b1 = -INFINITY, b2 = -INFINITY;
       const float *gk = &s_key[wave][lane * gsz];
+#pragma unroll 8
       for (int i = 0; i < gsz; ++i) {
         const float v = gk[i];
         if (v > b1) {
@@ -123,7 +167,7 @@ __global__ __launch_bounds__(256) void gate_route_kernel(
     }
     int rank = 0;
     for (int g = 0; g < G; ++g) {
-      const float o = __shfl(gs, g);
+      const float o = lane_f32(gs, g);
       rank += (o > gs) || (o == gs && g < lane);
     }
     keep = __ballot(lane < G && rank < TG);
@@ -152,7 +196,7 @@ __global__ __launch_bounds__(256) void gate_route_kernel(
 
   // ascending expert order: lane r (< K) holds the r-th pick; place it by rank
   int pos = 0;
-  for (int r = 0; r < K; ++r) pos += __shfl(mine, r) < mine;
+  for (int r = 0; r < K; ++r) pos += __builtin_amdgcn_readlane(mine, r) < mine;
   // step 5: unbiased scores at the chosen experts, renormalised, scaled
   float val = lane < K ? s_score[wave][mine] : 0.0f;
   if (lane < K) s_w[wave][pos] = val;
@@ -199,8 +243,8 @@ hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logi
 // A GEMM tile would leave most CUs idle here.  Each workgroup takes 4 expert
 // rows; its 8 wavefronts split K eight ways and form the dot products of up to
 // 8 tokens per pass in fp32 (lanes stride over their K range in 16-byte
-// pieces), reduce across lanes with a butterfly, then across wavefronts in LDS
-// in a fixed order.
+// pieces), sum the 16 lanes of each row with DPP moves, then add the rows and
+// wavefronts in LDS in a fixed order.
 namespace moe {
 namespace {
 
@@ -219,7 +263,7 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4_t v, float (&f)[8]) {
 __global__ __launch_bounds__(64 * kGemvWaves) void gate_logits_gemv_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg, int T, int E, int K,
     float *__restrict__ logits) {
-  __shared__ float part[kGemvWaves][kGemvExperts * kGemvTokens];
+  __shared__ float part[kGemvWaves][4][kGemvExperts * kGemvTokens];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e0 = blockIdx.x * kGemvExperts;
   const int units = K / 8;                                    // 16-byte pieces per row
@@ -233,37 +277,44 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gate_logits_gemv_kernel(
       for (int t = 0; t < kGemvTokens; ++t) acc[j][t] = 0.0f;
     for (int u = u0 + lane; u < u1; u += 64) {
       const int k = u * 8;
+      // every load is issued before the first use: rows past the last expert or
+      // token are clamped to a valid row and their sums are never stored
+      u32x4_t wr[kGemvExperts], xr[kGemvTokens];
+#pragma unroll
+      for (int j = 0; j < kGemvExperts; ++j)
+        wr[j] = *reinterpret_cast<const u32x4_t *>(wg + static_cast<int64_t>(min(e0 + j, E - 1)) * K + k);
+#pragma unroll
+      for (int t = 0; t < kGemvTokens; ++t)
+        xr[t] = *reinterpret_cast<const u32x4_t *>(x + static_cast<int64_t>(t0 + min(t, nt - 1)) * K + k);
       float w[kGemvExperts][8];
 #pragma unroll
-      for (int j = 0; j < kGemvExperts; ++j) {
-        if (e0 + j < E) bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(wg + static_cast<int64_t>(e0 + j) * K + k), w[j]);
-        else for (int i = 0; i < 8; ++i) w[j][i] = 0.0f;
-      }
+      for (int j = 0; j < kGemvExperts; ++j) bf16x8_to_f32(wr[j], w[j]);
 #pragma unroll
       for (int t = 0; t < kGemvTokens; ++t) {
-        if (t < nt) {
-          float xv[8];
-          bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(x + static_cast<int64_t>(t0 + t) * K + k), xv);
+        float xv[8];
+        bf16x8_to_f32(xr[t], xv);
 #pragma unroll
-          for (int j = 0; j < kGemvExperts; ++j)
+        for (int j = 0; j < kGemvExperts; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[j][t] = fmaf(w[j][i], xv[i], acc[j][t]);
-        }
+          for (int i = 0; i < 8; ++i) acc[j][t] = fmaf(w[j][i], xv[i], acc[j][t]);
       }
     }
+    // per-row sums by DPP; one lane per row stores them; then each output adds
+    // its 8 wavefronts x 4 rows in a fixed order
 #pragma unroll
     for (int j = 0; j < kGemvExperts; ++j)
 #pragma unroll
       for (int t = 0; t < kGemvTokens; ++t) {
-        float v = acc[j][t];
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0) part[wave][j * kGemvTokens + t] = v;
+        const float v = row_sum_f32(acc[j][t]);
+        if ((lane & 15) == 0) part[wave][lane >> 4][j * kGemvTokens + t] = v;
       }
     __syncthreads();
     if (threadIdx.x < kGemvExperts * kGemvTokens) {
       const int j = threadIdx.x / kGemvTokens, t = threadIdx.x % kGemvTokens;
       float v = 0.0f;
-      for (int w = 0; w < kGemvWaves; ++w) v += part[w][threadIdx.x];   // K order
+      for (int w = 0; w < kGemvWaves; ++w)   // K order
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v += part[w][r][threadIdx.x];
       if (t < nt && e0 + j < E) logits[static_cast<int64_t>(t0 + t) * E + e0 + j] = v;
     }
     __syncthreads();

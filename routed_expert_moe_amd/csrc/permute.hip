@@ -12,7 +12,7 @@
 //               counts, padded expert offsets, tile lists and -1 padding rows.
 //   3. scatter: row = expert_off[e] + base[blk][e] + rank.
 // With a single count workgroup (T*K <= 2048) the three phases run in one
-// launch.  Every value is computed without atomics, so the result is unique.
+// launch that keeps its intermediate tables in LDS.  Every value is computed without atomics, so the result is unique.
 #include "common.hpp"
 
 namespace moe {
@@ -55,7 +55,7 @@ __device__ void count_block(const PermArgs &a, int blk, int (*s_cnt)[kMaxE]) {
     int rank = 0, same = 0;
     while (todo) {
       const int leader = __ffsll(static_cast<long long>(todo)) - 1;
-      const int el = __shfl(e, leader);
+      const int el = __builtin_amdgcn_readlane(e, leader);   // leader is wavefront-uniform
       const uint64_t m = __ballot(e == el);
       if (e == el) {
         rank = __popcll(m & below);
@@ -164,16 +164,104 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(PermArgs 
   scatter_range(a, p, p + 1, 1);
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_fused_kernel(PermArgs a) {
-  __shared__ int s_cnt[kPermWaves][kMaxE];
-  __shared__ int s_pad[kMaxE];
-  count_block(a, 0, s_cnt);
+// All three phases in one workgroup for P <= kPairsPerBlock, with ranks,
+// histograms and offsets kept in LDS: the expert ids are read once and
+// nothing written here is read back from global memory.
+__global__ __launch_bounds__(kPermThreads) void permute_small_kernel(PermArgs a) {
+  __shared__ int s_cnt[kPermWaves][kMaxE];   // per-wavefront counts, then per-wavefront bases
+  __shared__ int s_tot[kMaxE];               // pairs per expert
+  __shared__ int s_end[kMaxE];               // padded sizes, then inclusive padded ends
+  __shared__ int s_rank[kPairsPerBlock];     // rank among the wavefront's pairs of one expert
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < kPermWaves * kMaxE; i += kPermThreads) (&s_cnt[0][0])[i] = 0;
+  constexpr int kChunks = kPairsPerWave / 64;
+  const int64_t base = static_cast<int64_t>(wave) * kPairsPerWave;
+  int ex[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {   // every load issues before the first use
+    const int64_t p = base + c * 64 + lane;
+    const int e = a.idx[p < a.P ? p : 0];
+    ex[c] = (p < a.P && e >= 0 && e < a.E) ? e : -1;
+  }
   __syncthreads();
-  __threadfence_block();
-  scan_all(a, s_pad);
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int e = ex[c];
+    uint64_t todo = __ballot(e >= 0);
+    int rank = 0, same = 0;
+    while (todo) {
+      const int leader = __ffsll(static_cast<long long>(todo)) - 1;
+      const int el = __builtin_amdgcn_readlane(e, leader);   // leader is wavefront-uniform
+      const uint64_t m = __ballot(e == el);
+      if (e == el) {
+        rank = __popcll(m & below);
+        same = __popcll(m);
+      }
+      todo &= ~m;
+    }
+    int r = 0;
+    if (e >= 0) r = s_cnt[wave][e] + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && rank == same - 1) s_cnt[wave][e] += same;
+    __builtin_amdgcn_wave_barrier();
+    s_rank[wave * kPairsPerWave + c * 64 + lane] = r;
+  }
   __syncthreads();
-  __threadfence_block();
-  scatter_range(a, threadIdx.x, a.P, kPermThreads);
+  for (int e = threadIdx.x; e < kMaxE; e += kPermThreads) {
+    int run = 0;
+    if (e < a.E) {
+#pragma unroll
+      for (int w = 0; w < kPermWaves; ++w) {
+        const int v = s_cnt[w][e];
+        s_cnt[w][e] = run;
+        run += v;
+      }
+      a.counts[e] = run;
+    }
+    s_tot[e] = run;
+    s_end[e] = (run + a.TM - 1) / a.TM * a.TM;
+  }
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {   // inclusive scan, two entries per thread
+    int v0 = 0, v1 = 0;
+    const int i0 = threadIdx.x, i1 = threadIdx.x + kPermThreads;
+    if (i0 >= off) v0 = s_end[i0 - off];
+    if (i1 >= off) v1 = s_end[i1 - off];
+    __syncthreads();
+    s_end[i0] += v0;
+    s_end[i1] += v1;
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < a.E; e += kPermThreads) {
+    const int end = s_end[e];
+    const int start = e > 0 ? s_end[e - 1] : 0;
+    a.expert_off[e] = start;
+    for (int j = 0; j < (end - start) / a.TM; ++j) {
+      a.tile_expert[start / a.TM + j] = e;
+      a.tile_row[start / a.TM + j] = start + j * a.TM;
+    }
+    for (int r = start + s_tot[e]; r < end; ++r) a.sorted_pair[r] = -1;
+  }
+  if (threadIdx.x == 0) {
+    a.expert_off[a.E] = s_end[a.E - 1];
+    *a.n_tiles = s_end[a.E - 1] / a.TM;
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int64_t p = base + c * 64 + lane;
+    if (p < a.P) {
+      const int e = ex[c];
+      if (e < 0) {
+        a.pair_row[p] = -1;
+      } else {
+        const int start = e > 0 ? s_end[e - 1] : 0;
+        const int row = start + s_cnt[wave][e] + s_rank[wave * kPairsPerWave + c * 64 + lane];
+        a.sorted_pair[row] = static_cast<int32_t>(p);
+        a.pair_row[p] = row;
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -201,7 +289,7 @@ hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_
   a.local_rank = r.scratch;
   a.hist = r.scratch + a.P;
   if (a.nblk == 1) {
-    hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(kPermThreads), 0, st, a);
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, st, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(permute_count_kernel, dim3(a.nblk), dim3(kPermThreads), 0, st, a);

@@ -287,6 +287,10 @@ def test_combine_one_hot_selects_rows():
     B.moe_combine(cfg, T, None, z, y, r, torch.zeros(T, K, device="cuda"), out)
     torch.cuda.synchronize()
     assert torch.equal(out, z)
+    # no residual, no shared term, one-hot weights: exactly the selected rows
+    B.moe_combine(cfg, T, None, None, y, r, onehot.cuda(), out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, y[torch.as_tensor(rows, device="cuda").long()])
 
 
 def test_imbalanced_routing_many_tiles():
