@@ -178,6 +178,29 @@ def time_pass(p: Pass, steps: int, warmup: int):
     return total_ms, up_ms, wall
 
 
+def time_bias_update(p: Pass, shape, calls: int = 200):
+    """The auxiliary-loss-free bias update on the routing of the last timed batch.
+
+    A training-time step after the gate: E counts and E biases in, E biases out,
+    one tiny launch, so it is bound by launch latency, not by a roofline."""
+    import torch
+    B = p.B
+    bias = p.layer.bias.clone()
+    for _ in range(10):
+        B.moe_bias_update(p.cfg, p.T, p.r, 1e-3, bias)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(calls):
+        B.moe_bias_update(p.cfg, p.T, p.r, 1e-3, bias)
+    b.record()
+    torch.cuda.synchronize()
+    return {"what": "moe_bias_update (auxiliary-loss-free balancing step) on this batch's routing",
+            "us_per_call": a.elapsed_time(b) / calls * 1e3, "experts": shape.n_routed,
+            "bound": "launch latency", "bytes_per_call": shape.n_routed * 12}
+
+
 def cpu_baseline(layer, n_tokens: int):
     """The float64 oracle on the first n_tokens tokens of the same workload, on host cores."""
     import numpy as np
@@ -255,6 +278,7 @@ def main():
                              "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)"),
         "wall_s": wall,
     }
+    res["bias_update"] = time_bias_update(p, shape)
     del p
     torch.cuda.empty_cache()
 

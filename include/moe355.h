@@ -206,6 +206,21 @@ moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const mo
                        void *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* Auxiliary-loss-free load balancing, one step (DeepSeek-V3 notes page,
+ * "V3 improvement 1": b_i follows each expert's load at speed gamma; DeepSeek-R1
+ * analysis page, MoE hyper-parameters paragraph: an overloaded expert's bias is
+ * lowered, an underloaded expert's raised).  With load_e = r->counts[e], the
+ * pairs of this batch routed to expert e by moe_permute:
+ *   bias[e] -= gamma  if load_e * n_routed > T * top_k   (above the mean load)
+ *   bias[e] += gamma  if load_e * n_routed < T * top_k   (below it)
+ * and an expert exactly at the mean keeps its bias bit for bit.  The comparison
+ * is exact (integers); the update is one fp32 addition.
+ *   r: the routing moe_permute filled for this T (device counts are read)
+ *   bias [n_routed] fp32, device, updated in place (the gate's `bias` input)
+ *   gamma: finite, >= 0.  T = 0 is a no-op. */
+moe_status moe_bias_update(const moe_config *cfg, int64_t T, const moe_routing *r, float gamma,
+                           float *bias, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,7 +61,7 @@ class moe_routing(ctypes.Structure):
 
 EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspace_size",
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
-            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward")
+            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update")
 
 _lib = None
 
@@ -91,6 +91,7 @@ def lib():
                             P, P, P, P, P],
         "moe_combine": [cfgp, I64, P, P, P, ctypes.POINTER(moe_routing), P, P, P],
         "moe_forward": [cfgp, I64, P, ctypes.POINTER(moe_weights), P, P, P, P, SZ, P],
+        "moe_bias_update": [cfgp, I64, ctypes.POINTER(moe_routing), ctypes.c_float, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -227,6 +228,11 @@ def moe_combine(cfg: moe_config, T: int, u, z, y_pairs, routing: Routing, topk_w
                 stream=None) -> None:
     _check(lib().moe_combine(ctypes.byref(cfg), T, _ptr(u), _ptr(z), _ptr(y_pairs),
                              ctypes.byref(routing.struct), _ptr(topk_w), _ptr(out), _stream(stream)))
+
+
+def moe_bias_update(cfg: moe_config, T: int, routing: Routing, gamma: float, bias, stream=None) -> None:
+    _check(lib().moe_bias_update(ctypes.byref(cfg), T, ctypes.byref(routing.struct), float(gamma),
+                                 _ptr(bias), _stream(stream)))
 
 
 def moe_forward(cfg: moe_config, T: int, x, weights: moe_weights, out, topk_idx=None, topk_w=None,

@@ -480,6 +480,20 @@ moe_status moe_combine(const moe_config *cfg, int64_t T, const void *u, const vo
   return ok();
 }
 
+moe_status moe_bias_update(const moe_config *cfg, int64_t T, const moe_routing *r, float gamma,
+                           float *bias, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (!isfinite(gamma) || !(gamma >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite and >= 0");
+  if (bias == nullptr) return fail(MOE_ERR_INVALID_ARG, "bias is NULL");
+  if (reinterpret_cast<uintptr_t>(bias) % 4 != 0) return fail(MOE_ERR_INVALID_ARG, "bias is not 4-byte aligned");
+  MOE_TRY(check_routing(*cfg, T, r));
+  if (T == 0) return ok();
+  const hipError_t e = launch_bias_update(*cfg, T, *r, gamma, bias, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "bias update launch");
+  return ok();
+}
+
 moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
                        void *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                        void *stream) {

@@ -76,6 +76,8 @@ hipError_t launch_gate_logits_gemv(const moe_config &cfg, int64_t T, const void 
                                    const void *w_gate, float *logits, hipStream_t st);
 hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_idx,
                           const moe_routing &r, hipStream_t st);
+hipError_t launch_bias_update(const moe_config &cfg, int64_t T, const moe_routing &r, float gamma,
+                              float *bias, hipStream_t st);
 hipError_t launch_combine(const moe_config &cfg, int64_t T, const void *u, const void *z,
                           const void *y, const moe_routing &r, const float *w, void *out,
                           hipStream_t st);

@@ -105,10 +105,9 @@ def make_x(shape: LayerShape, device, T: Optional[int] = None, seed_offset: int 
     return _normal((T, shape.dim), 1.0, device, g).to(_TORCH_ACT[shape.act])
 
 
-def make_layer(shape: LayerShape, device="cpu", T: Optional[int] = None,
-               shared: bool = True) -> LayerTensors:
-    """Draw every input of one layer call on `device` (x has T rows, default shape.T)."""
-    E, D, I, S = shape.n_routed, shape.dim, shape.inter_dim, shape.n_shared
+def make_gate_inputs(shape: LayerShape, device="cpu", T: Optional[int] = None):
+    """(x, w_gate, bias) of one layer call: the same draws make_layer makes."""
+    E, D = shape.n_routed, shape.dim
     act = _TORCH_ACT[shape.act]
     x = make_x(shape, device, T)
 
@@ -121,6 +120,14 @@ def make_layer(shape: LayerShape, device="cpu", T: Optional[int] = None,
     if shape.bias_range is not None:
         g = _gen(device, shape.seed, "bias")
         bias = (torch.rand((E,), generator=g, device=device, dtype=torch.float32) * 2.0 - 1.0) * shape.bias_range
+    return x, w_gate, bias
+
+
+def make_layer(shape: LayerShape, device="cpu", T: Optional[int] = None,
+               shared: bool = True) -> LayerTensors:
+    """Draw every input of one layer call on `device` (x has T rows, default shape.T)."""
+    E, D, I, S = shape.n_routed, shape.dim, shape.inter_dim, shape.n_shared
+    x, w_gate, bias = make_gate_inputs(shape, device, T)
 
     w13_parts, w13_sc, w2_parts, w2_sc = [], [], [], []
     for e in range(E):

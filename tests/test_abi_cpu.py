@@ -113,6 +113,21 @@ def test_entry_points_validate_before_launch():
     assert L.moe_forward(ctypes.byref(c8), 8, fake, ctypes.byref(w), fake + 256, None, None, fake, need8, None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_bias_update_validates_before_launch():
+    c = _cfg()
+    L = B.lib()
+    fake = 1 << 20
+    r = B.moe_routing_init(c, 64, fake, B.moe_routing_size(c, 64))
+    for gamma in (float("nan"), float("inf"), -1e-3):
+        assert L.moe_bias_update(ctypes.byref(c), 64, ctypes.byref(r), gamma, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(ctypes.byref(c), 64, ctypes.byref(r), 1e-3, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(ctypes.byref(c), 64, ctypes.byref(r), 1e-3, fake + 2, None) == B.MOE_ERR_INVALID_ARG
+    # routing built for another T
+    assert L.moe_bias_update(ctypes.byref(c), 32, ctypes.byref(r), 1e-3, fake, None) == B.MOE_ERR_INVALID_ARG
+    r0 = B.moe_routing_init(c, 0, fake, B.moe_routing_size(c, 0))
+    assert L.moe_bias_update(ctypes.byref(c), 0, ctypes.byref(r0), 1e-3, fake, None) == B.MOE_OK
+
+
 def test_T_zero_is_a_no_op():
     c = _cfg()
     L = B.lib()

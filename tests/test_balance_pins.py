@@ -60,8 +60,10 @@ def test_direction_and_balanced_experts():
         new = balance.bias_update(bias, loads, T, K, gamma)
         mean = T * K / E
         for e in range(E):
-            if loads[e] == mean or gamma == 0.0:
+            if loads[e] == mean:
                 assert new[e].view(np.uint32) == bias[e].view(np.uint32)
+            elif gamma == 0.0:
+                assert new[e] == bias[e]
             elif loads[e] > mean:
                 assert new[e] < bias[e] and abs(float(new[e]) - (float(bias[e]) - gamma)) <= 1e-7
             else:
