@@ -28,6 +28,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 # Measured HBM traffic per launch of the two roofline kernels: rocprofv3 --pmc
@@ -67,21 +68,22 @@ def measured_traffic(key: str):
     return (c["fetch_kib"] * FETCH_SCALE + c["write_kib"] * WRITE_SCALE) * 1024.0
 
 
-def roofline(flops: float, nbytes: float, ms: float, traffic, kernel: str) -> dict:
+def roofline(flops: float, nbytes: float, ms: float, traffic, kernel: str,
+             peak_tflops: float = PEAK_BF16_TFLOPS) -> dict:
     """The binding ceiling of a kernel: MFMA if its flops take longer at peak than its bytes, else HBM."""
-    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_mfma = flops / (peak_tflops * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     tflops = flops / (ms / 1e3) / 1e12
     gbs = nbytes / (ms / 1e3) / 1e9
     r = {"kernel": kernel}
     if t_mfma >= t_hbm:
-        r.update(bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                 frac=tflops / PEAK_BF16_TFLOPS)
+        r.update(bound="mfma", achieved=tflops, peak=peak_tflops, unit="TFLOP/s",
+                 frac=tflops / peak_tflops)
     else:
         r.update(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s", frac=gbs / PEAK_HBM_GBS)
     r.update(traffic=traffic, traffic_unit="bytes per launch (HBM, measured)",
              avg_launch_ms=ms, algorithmic_flops=flops, algorithmic_bytes=nbytes,
-             mfma_frac=tflops / PEAK_BF16_TFLOPS, hbm_frac=gbs / PEAK_HBM_GBS)
+             mfma_frac=tflops / peak_tflops, hbm_frac=gbs / PEAK_HBM_GBS)
     return r
 
 
@@ -128,6 +130,8 @@ class Pass:
         B, L = self.B, self.layer
         B.moe_gate(self.cfg, self.T, L.x, L.w_gate, L.bias, self.logits, self.idx, self.tw)
         B.moe_permute(self.cfg, self.T, self.idx, self.r)
+        if self.cfg.act_quant:
+            B.moe_quant_act(self.cfg, self.T, L.x, self.r)
         if ev_up is not None:
             ev_up[0].record()
         B.moe_expert_up(self.cfg, self.T, L.x, self.r, self.w, self.h, self.hs)
@@ -280,6 +284,27 @@ def main():
     }
     res["bias_update"] = time_bias_update(p, shape)
     del p
+    torch.cuda.empty_cache()
+
+    # ---- the same prefill batch in FP8 W8A8 (fp8 weights, activations quantised 1x128)
+    wshape = configs.V3_PREFILL_W8A8
+    wlayer = synth.make_layer(wshape, device="cuda")
+    wp = Pass(wlayer)
+    wtotal_ms, wup_ms, _ = time_pass(wp, args.steps, args.warmup)
+    wfig = work_figures(wlayer, wp.r.counts.cpu().numpy())
+    wms = wtotal_ms / args.steps
+    res["prefill_w8a8"] = {
+        "workload": wshape.name, "T": wshape.T,
+        "dtype": "fp8-e4m3 weights (128x128 fp32 scales) x fp8-e4m3 activations (1x128 fp32 scales)",
+        "ms_per_step": wms, "tokens_per_s": wshape.T * args.steps / (wtotal_ms / 1e3),
+        "experts_touched": wfig["touched"],
+        "layer_tflops": wfig["flops_layer"] / (wms / 1e3) / 1e12,
+        "layer_mfma_frac_fp8": wfig["flops_layer"] / (wms / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
+        "roofline": roofline(wfig["flops_up"], wfig["bytes_up"], wup_ms, None,
+                             "moe_expert_up (fp8 x fp8 grouped GEMM + SwiGLU + h quantisation, gemm_fp8_kernel)",
+                             PEAK_FP8_TFLOPS),
+    }
+    del wp, wlayer
     torch.cuda.empty_cache()
 
     # ---- decode: 8 tokens, fp8 expert weights

@@ -80,6 +80,12 @@ typedef struct moe_config {
   int32_t weight_dtype;  /* routed + shared expert weights: MOE_F32 (with act F32), MOE_BF16 or
                             MOE_FP8_E4M3_B128 (with act BF16) */
   int32_t add_residual;  /* 1: out includes u_t (the total-output equation); 0: out = FFN terms only */
+  int32_t act_quant;     /* 0: the expert GEMMs read activations in act dtype (W8A16 with fp8
+                            weights); 1: FP8 W8A8 (KTransformers DeepSeek page, expert formats):
+                            x and the SwiGLU output h are quantised to e4m3 with one fp32 scale
+                            per row per 128 columns, s = max|a|/448 (1 for a zero block),
+                            code = round-to-nearest-even(a/s), right before each expert GEMM.
+                            Requires act BF16 and weights FP8_E4M3_B128. */
 } moe_config;
 
 /* Expert weights.  fp8 scale tensors are fp32 with one entry per 128x128 block
@@ -115,6 +121,8 @@ typedef struct moe_routing {
   int32_t *tile_row;     /* [max_tiles]  first row of each tile */
   int32_t *n_tiles;      /* [1]          tiles in use */
   int32_t *scratch;      /* internal */
+  uint8_t *act_q;        /* act_quant only (else NULL): [T, D] e4m3 codes of x, from moe_quant_act */
+  float *act_s;          /* act_quant only (else NULL): [T, D/128] fp32 scales of act_q */
 } moe_routing;
 
 /* ---- host-only queries (no device access) -------------------------------- */
@@ -172,7 +180,12 @@ moe_status moe_permute(const moe_config *cfg, int64_t T, const int32_t *topk_idx
  *   hs[t] = silu(SW1 x_t) * (SW3 x_t)  [T, S*I];  z[t] = SW2 hs[t]  [T, D]  act dtype
  * Accumulation is fp32; h, hs, y_pairs and z are rounded once to the act dtype.
  * Padding rows of h and y_pairs hold unspecified values.  r must hold the
- * output of moe_permute for the same T and topk_idx. */
+ * output of moe_permute for the same T and topk_idx.
+ * With act_quant = 1 the GEMMs read x as r->act_q / r->act_s (moe_quant_act),
+ * and h / hs hold the SwiGLU output quantised from fp32 in the same 1 x 128
+ * format, inside the same buffers: R*C e4m3 codes ([R, C] with R = max_rows,
+ * C = I for h; R = T, C = S*I for hs), then at byte offset (R*C rounded up to
+ * 256) the fp32 scales [R, C/128].  y_pairs and z stay bf16. */
 moe_status moe_expert_ffn(const moe_config *cfg, int64_t T, const void *x,
                           const moe_routing *r, const moe_weights *w, void *h, void *y_pairs,
                           void *hs, void *z, void *stream);
@@ -186,6 +199,13 @@ moe_status moe_expert_up(const moe_config *cfg, int64_t T, const void *x, const 
 moe_status moe_expert_down(const moe_config *cfg, int64_t T, const moe_routing *r,
                            const moe_weights *w, const void *h, const void *hs, void *y_pairs,
                            void *z, void *stream);
+
+/* FP8 W8A8 only (cfg->act_quant = 1): quantise x for the expert GEMMs into
+ * r->act_q / r->act_s (1 x 128 blocks, the rule stated at moe_config.act_quant).
+ * Call it after moe_routing_init and before moe_expert_up / moe_expert_ffn for
+ * the same x; moe_forward calls it itself.  x [T, D] bf16. */
+moe_status moe_quant_act(const moe_config *cfg, int64_t T, const void *x, const moe_routing *r,
+                         void *stream);
 
 /* Combine (total-output equation): for every token t
  *   out[t] = (add_residual ? u[t] : 0) + (z ? z[t] : 0)

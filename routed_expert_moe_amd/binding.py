@@ -43,7 +43,7 @@ class moe_config(ctypes.Structure):
                 ("inter_dim", ctypes.c_int32), ("route_scale", ctypes.c_float),
                 ("score_func", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("add_residual", ctypes.c_int32)]
+                ("add_residual", ctypes.c_int32), ("act_quant", ctypes.c_int32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -56,12 +56,14 @@ class moe_routing(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("max_rows", ctypes.c_int32),
                 ("max_tiles", ctypes.c_int32), ("pad_", ctypes.c_int32)] + \
                [(n, ctypes.c_void_p) for n in ("counts", "expert_off", "sorted_pair", "pair_row",
-                                               "tile_expert", "tile_row", "n_tiles", "scratch")]
+                                               "tile_expert", "tile_row", "n_tiles", "scratch",
+                                               "act_q", "act_s")]
 
 
 EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspace_size",
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
-            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update")
+            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update",
+            "moe_quant_act")
 
 _lib = None
 
@@ -92,6 +94,7 @@ def lib():
         "moe_combine": [cfgp, I64, P, P, P, ctypes.POINTER(moe_routing), P, P, P],
         "moe_forward": [cfgp, I64, P, ctypes.POINTER(moe_weights), P, P, P, P, SZ, P],
         "moe_bias_update": [cfgp, I64, ctypes.POINTER(moe_routing), ctypes.c_float, P, P],
+        "moe_quant_act": [cfgp, I64, P, ctypes.POINTER(moe_routing), P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -130,7 +133,7 @@ def config_of(shape: LayerShape) -> moe_config:
                       inter_dim=shape.inter_dim, route_scale=shape.route_scale,
                       score_func=_SCORE[shape.score], norm_topk=shape.norm_topk,
                       act_dtype=_DTYPE[shape.act], weight_dtype=_DTYPE[shape.weight],
-                      add_residual=shape.add_residual)
+                      add_residual=shape.add_residual, act_quant=shape.act_quant)
 
 
 def weights_of(layer) -> moe_weights:
@@ -175,6 +178,8 @@ class Routing:
     tile_expert: torch.Tensor
     tile_row: torch.Tensor
     n_tiles: torch.Tensor
+    act_q: Optional[torch.Tensor] = None     # act_quant: [T, D] e4m3 codes (uint8)
+    act_s: Optional[torch.Tensor] = None     # act_quant: [T, D/128] fp32 scales
 
 
 def make_routing(cfg: moe_config, T: int, device="cuda") -> Routing:
@@ -187,9 +192,15 @@ def make_routing(cfg: moe_config, T: int, device="cuda") -> Routing:
         off = ptr - base
         return buf[off: off + 4 * n].view(torch.int32)
     P = T * cfg.top_k
+    act_q = act_s = None
+    if cfg.act_quant and T > 0:
+        nb = cfg.dim // 128
+        act_q = buf[r.act_q - base: r.act_q - base + T * cfg.dim].view(T, cfg.dim)
+        act_s = buf[r.act_s - base: r.act_s - base + 4 * T * nb].view(torch.float32).view(T, nb)
     return Routing(r, buf, view(r.counts, cfg.n_routed), view(r.expert_off, cfg.n_routed + 1),
                    view(r.sorted_pair, r.max_rows), view(r.pair_row, P),
-                   view(r.tile_expert, r.max_tiles), view(r.tile_row, r.max_tiles), view(r.n_tiles, 1))
+                   view(r.tile_expert, r.max_tiles), view(r.tile_row, r.max_tiles), view(r.n_tiles, 1),
+                   act_q, act_s)
 
 
 # ---- the forward pass, step by step ---------------------------------------------
@@ -228,6 +239,10 @@ def moe_combine(cfg: moe_config, T: int, u, z, y_pairs, routing: Routing, topk_w
                 stream=None) -> None:
     _check(lib().moe_combine(ctypes.byref(cfg), T, _ptr(u), _ptr(z), _ptr(y_pairs),
                              ctypes.byref(routing.struct), _ptr(topk_w), _ptr(out), _stream(stream)))
+
+
+def moe_quant_act(cfg: moe_config, T: int, x, routing: Routing, stream=None) -> None:
+    _check(lib().moe_quant_act(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(routing.struct), _stream(stream)))
 
 
 def moe_bias_update(cfg: moe_config, T: int, routing: Routing, gamma: float, bias, stream=None) -> None:

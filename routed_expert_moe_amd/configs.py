@@ -42,6 +42,7 @@ class LayerShape:
     weight: str                # expert weight storage: "f32" | "bf16" | "fp8"
     norm_topk: int = -1        # -1: sigmoid renormalises, softmax does not
     add_residual: int = 1
+    act_quant: int = 0         # 1: FP8 W8A8 (activations quantised 1x128 before the expert GEMMs)
     # --- synthetic input recipe ---
     seed: int = 0
     bias_range: Optional[float] = None   # per-expert bias ~ U(-r, r); None = no bias
@@ -80,5 +81,12 @@ V3_DECODE_FP8 = LayerShape(
     topk_groups=4, top_k=8, n_shared=1, inter_dim=2048, score=SCORE_SIGMOID,
     route_scale=2.5, act="bf16", weight="fp8", seed=4, bias_range=0.05)
 
-ALL = [TINY_F32, V2_LITE_BF16, V2_BF16, V3_PREFILL_BF16, V3_DECODE_FP8]
+# The V3 prefill batch with the released checkpoint's fp8 expert weights and the
+# W8A8 expert format (a next step after the bf16 and decode workloads).
+V3_PREFILL_W8A8 = LayerShape(
+    name="v3_prefill_w8a8_T8192", T=8192, dim=7168, n_routed=256, n_groups=8,
+    topk_groups=4, top_k=8, n_shared=1, inter_dim=2048, score=SCORE_SIGMOID,
+    route_scale=2.5, act="bf16", weight="fp8", act_quant=1, seed=5, bias_range=0.05)
+
+ALL = [TINY_F32, V2_LITE_BF16, V2_BF16, V3_PREFILL_BF16, V3_DECODE_FP8, V3_PREFILL_W8A8]
 BY_NAME = {c.name: c for c in ALL}

@@ -43,6 +43,7 @@ size_t weight_bytes(const moe_config &c) {
 
 Plan plan_for(const moe_config &c, int64_t T) {
   if (c.act_dtype == MOE_F32) return Plan{PATH_F32, kF32TileM};
+  if (c.act_quant) return Plan{PATH_FP8, kMfmaTileM};
   if (c.weight_dtype == MOE_FP8_E4M3_B128) return Plan{PATH_SKINNY, kSkinnyTileM};
   const int64_t avg_rows = T * c.top_k / c.n_routed;
   if (avg_rows < 32) return Plan{PATH_SKINNY, kSkinnyTileM};
@@ -53,7 +54,7 @@ struct RoutingLayout {
   int tile_m;
   int64_t max_rows, max_tiles, P;
   size_t off_counts, off_expert_off, off_sorted, off_pair_row, off_tile_expert, off_tile_row,
-      off_ntiles, off_scratch, total;
+      off_ntiles, off_scratch, off_act_q, off_act_s, total;
 };
 
 RoutingLayout routing_layout(const moe_config &c, int64_t T) {
@@ -77,6 +78,10 @@ RoutingLayout routing_layout(const moe_config &c, int64_t T) {
   L.off_tile_row = take(4 * static_cast<size_t>(L.max_tiles));
   L.off_ntiles = take(4);
   L.off_scratch = take(4 * static_cast<size_t>(permute_scratch_ints(L.P, c.n_routed)));
+  if (c.act_quant) {   // fp8 codes of x and their 1 x 128 scales
+    L.off_act_q = take(static_cast<size_t>(T) * c.dim);
+    L.off_act_s = take(4 * static_cast<size_t>(T) * (c.dim / 128));
+  }
   L.total = o;
   return L;
 }
@@ -142,6 +147,14 @@ moe_status check_cfg(const moe_config *c) {
   if (c->dim % 8 != 0 || c->inter_dim % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "dim and inter_dim must be multiples of 8");
   if (c->weight_dtype == MOE_FP8_E4M3_B128 && (c->dim % 128 != 0 || c->inter_dim % 128 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "fp8 block scales need dim and inter_dim multiples of 128");
+  if (c->act_quant != 0 && c->act_quant != 1) return fail(MOE_ERR_INVALID_ARG, "act_quant must be 0 or 1");
+  if (c->act_quant) {
+    if (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_FP8_E4M3_B128)
+      return fail(MOE_ERR_UNSUPPORTED, "act_quant needs bf16 activations and fp8 weights");
+    // the fp8 GEMM keeps one weight row's block scales in two registers per lane
+    if (c->dim > 16384 || static_cast<int64_t>(c->inter_dim) * (c->n_shared > 0 ? c->n_shared : 1) > 16384)
+      return fail(MOE_ERR_UNSUPPORTED, "act_quant supports reduction lengths (dim, n_shared*inter_dim) up to 16384");
+  }
   return MOE_OK;
 }
 
@@ -150,6 +163,11 @@ moe_status check_T(const moe_config &c, int64_t T) {
   const int64_t rows = T * c.top_k + static_cast<int64_t>(c.n_routed) * 128;
   if (T > (1ll << 31) / 64 || rows >= (1ll << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T too large for 32-bit row indices");
+  if (c.act_quant) {   // the fp8 GEMM addresses its operands with 32-bit byte offsets
+    const int64_t SI = static_cast<int64_t>(c.n_shared) * c.inter_dim;
+    if (T * c.dim >= (1ll << 31) || rows * c.inter_dim >= (1ll << 31) || T * SI >= (1ll << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "act_quant: activation matrices must stay below 2 GiB");
+  }
   return MOE_OK;
 }
 
@@ -185,6 +203,8 @@ moe_status check_routing(const moe_config &c, int64_t T, const moe_routing *r) {
   if (!r->counts || !r->expert_off || !r->sorted_pair || !r->pair_row || !r->tile_expert ||
       !r->tile_row || !r->n_tiles || !r->scratch)
     return fail(MOE_ERR_INVALID_ARG, "routing has NULL arrays");
+  if (c.act_quant && (!r->act_q || !r->act_s))
+    return fail(MOE_ERR_INVALID_ARG, "routing was built without act_quant buffers");
   return MOE_OK;
 }
 
@@ -288,9 +308,40 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
     dn[1].ldc = D;
     dn[1].n_tiles_host = dense_tiles;
   }
+  if (p.path == PATH_FP8) {
+    // W8A8: gate/up read the fp8 codes of x (moe_quant_act) and leave h as fp8
+    // codes followed by their scales inside the h buffer; down reads them back
+    float *h_s = reinterpret_cast<float *>(static_cast<char *>(h) +
+                                           round_up(static_cast<size_t>(r.max_rows) * I, kAlign));
+    up[0].a = r.act_q;
+    up[0].lda = D;
+    up[0].a_scale = r.act_s;
+    up[0].a_sld = D / 128;
+    up[0].ldc = I;
+    up[0].c_scale = h_s;
+    up[0].c_sld = I / 128;
+    dn[0].lda = I;
+    dn[0].a_scale = h_s;
+    dn[0].a_sld = I / 128;
+    if (shared) {
+      float *hs_s = reinterpret_cast<float *>(static_cast<char *>(hs) +
+                                              round_up(static_cast<size_t>(T) * SI, kAlign));
+      up[1].a = r.act_q;
+      up[1].lda = D;
+      up[1].a_scale = r.act_s;
+      up[1].a_sld = D / 128;
+      up[1].ldc = SI;
+      up[1].c_scale = hs_s;
+      up[1].c_sld = SI / 128;
+      dn[1].lda = SI;
+      dn[1].a_scale = hs_s;
+      dn[1].a_sld = SI / 128;
+    }
+  }
   auto run = [&](Segment *segs, Epilogue epi) -> hipError_t {
     switch (p.path) {
       case PATH_F32: return launch_gemm_f32(segs, nseg, p.tile_m, epi, st);
+      case PATH_FP8: return launch_gemm_fp8(segs, nseg, epi, st);
       case PATH_MFMA:
         if (gemm_mfma2_supported(segs, nseg)) return launch_gemm_mfma2(segs, nseg, epi, false, st);
         return launch_gemm_mfma(segs, nseg, p.tile_m, epi, false, st);
@@ -362,6 +413,8 @@ moe_status moe_routing_init(const moe_config *cfg, int64_t T, void *buf, size_t 
   r->tile_row = reinterpret_cast<int32_t *>(b + L.off_tile_row);
   r->n_tiles = reinterpret_cast<int32_t *>(b + L.off_ntiles);
   r->scratch = reinterpret_cast<int32_t *>(b + L.off_scratch);
+  r->act_q = cfg->act_quant ? reinterpret_cast<uint8_t *>(b + L.off_act_q) : nullptr;
+  r->act_s = cfg->act_quant ? reinterpret_cast<float *>(b + L.off_act_s) : nullptr;
   return ok();
 }
 
@@ -480,6 +533,19 @@ moe_status moe_combine(const moe_config *cfg, int64_t T, const void *u, const vo
   return ok();
 }
 
+moe_status moe_quant_act(const moe_config *cfg, int64_t T, const void *x, const moe_routing *r,
+                         void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (!cfg->act_quant) return fail(MOE_ERR_INVALID_ARG, "moe_quant_act needs cfg->act_quant = 1");
+  MOE_NEED(x, "x");
+  MOE_TRY(check_routing(*cfg, T, r));
+  if (T == 0) return ok();
+  const hipError_t e = launch_quant_act(x, T, cfg->dim, r->act_q, r->act_s, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "activation quantisation launch");
+  return ok();
+}
+
 moe_status moe_bias_update(const moe_config *cfg, int64_t T, const moe_routing *r, float gamma,
                            float *bias, void *stream) {
   MOE_TRY(check_cfg(cfg));
@@ -522,6 +588,10 @@ moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const mo
   MOE_TRY(do_gate(c, T, x, w->w_gate, w->bias, logits, idx, wt, nullptr, st));
   hipError_t e = launch_permute(c, T, idx, r, st);
   if (e != hipSuccess) return device_fail(e, "permute launch");
+  if (c.act_quant) {
+    e = launch_quant_act(x, T, c.dim, r.act_q, r.act_s, st);
+    if (e != hipSuccess) return device_fail(e, "activation quantisation launch");
+  }
   const bool shared = c.n_shared > 0;
   void *h = b + W.off_h, *hs = b + W.off_hs, *y = b + W.off_y, *z = b + W.off_z;
   MOE_TRY(do_ffn(c, T, x, r, *w, h, y, shared ? hs : nullptr, shared ? z : nullptr, st));

@@ -52,6 +52,12 @@ struct Segment {
   int64_t ldc;            // elements
   // tiles: routed segments read the tile lists written by moe_permute; dense
   // segments cover rows [0, a_rows) in tiles of tile_m with expert 0.
+  // fp8 activations (W8A8): one fp32 scale per A row per 128 columns of K, and
+  // for fp8 output the scales written per C row per 128 output columns
+  const float *a_scale;   // [A rows, k/128] or nullptr
+  int64_t a_sld;          // floats between A rows' scales
+  float *c_scale;         // [C rows, out cols/128] or nullptr
+  int64_t c_sld;
   const int32_t *tile_row;
   const int32_t *tile_expert;
   const int32_t *expert_off;   // first row of each expert, multiples of tile_m (routed only)
@@ -62,7 +68,7 @@ struct Segment {
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1 };
 
 // plan chosen for (cfg, T)
-enum Path { PATH_F32 = 0, PATH_MFMA = 1, PATH_SKINNY = 2 };
+enum Path { PATH_F32 = 0, PATH_MFMA = 1, PATH_SKINNY = 2, PATH_FP8 = 3 };
 struct Plan {
   int path;
   int tile_m;
@@ -76,6 +82,12 @@ hipError_t launch_gate_logits_gemv(const moe_config &cfg, int64_t T, const void 
                                    const void *w_gate, float *logits, hipStream_t st);
 hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_idx,
                           const moe_routing &r, hipStream_t st);
+// fp8 x fp8 grouped GEMM (W8A8 experts): A codes with 1x128 scales, B codes with
+// 128x128 scales; EPI_SWIGLU writes fp8 codes + scales, EPI_STORE bf16.
+bool gemm_fp8_supported(const Segment *segs, int nseg);
+hipError_t launch_gemm_fp8(const Segment *segs, int nseg, Epilogue epi, hipStream_t st);
+hipError_t launch_quant_act(const void *x, int64_t rows, int64_t cols, uint8_t *q, float *s,
+                            hipStream_t st);
 hipError_t launch_bias_update(const moe_config &cfg, int64_t T, const moe_routing &r, float gamma,
                               float *bias, hipStream_t st);
 hipError_t launch_combine(const moe_config &cfg, int64_t T, const void *u, const void *z,

@@ -10,6 +10,7 @@ import numpy as np
 import torch
 
 import oracle
+from oracle import w8a8
 from routed_expert_moe_amd.configs import LayerShape
 
 
@@ -58,8 +59,9 @@ def bias_f64(layer):
 
 
 def run_oracle(layer, tokens=None, force_idx=None, x=None):
-    """Oracle forward of `layer` (optionally on another x and a token subset)."""
+    """Oracle forward of `layer` (optionally on another x and a token subset);
+    the fp8 W8A8 layer when the shape quantises its activations."""
     xx = to_f64(layer.x if x is None else x)
-    return oracle.moe_layer(xx, to_f64(layer.w_gate), bias_f64(layer), expert_fn(layer),
-                            shared_pair(layer), spec_of(layer.shape), tokens=tokens,
-                            force_idx=force_idx)
+    fn = w8a8.moe_layer_w8a8 if layer.shape.act_quant else oracle.moe_layer
+    return fn(xx, to_f64(layer.w_gate), bias_f64(layer), expert_fn(layer), shared_pair(layer),
+              spec_of(layer.shape), tokens=tokens, force_idx=force_idx)

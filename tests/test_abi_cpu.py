@@ -30,9 +30,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(B.moe_config) == 13 * 4
+    assert ctypes.sizeof(B.moe_config) == 14 * 4
     assert ctypes.sizeof(B.moe_weights) == 10 * 8
-    assert ctypes.sizeof(B.moe_routing) == 16 + 8 * 8
+    assert ctypes.sizeof(B.moe_routing) == 16 + 10 * 8
 
 
 @pytest.mark.parametrize("shape", configs.ALL, ids=lambda s: s.name)
