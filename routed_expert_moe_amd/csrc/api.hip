@@ -227,8 +227,11 @@ moe_status do_gate(const moe_config &c, int64_t T, const void *x, const void *w_
     e = launch_gemm_f32(&s, 1, kF32TileM, EPI_STORE, st);
   } else if (T >= 64) {
     s.n_tiles_host = static_cast<int32_t>((T + kMfmaTileM - 1) / kMfmaTileM);
-    e = gemm_mfma2_supported(&s, 1) ? launch_gemm_mfma2(&s, 1, EPI_STORE, true, st)
-                                    : launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
+    // with few experts the 512-wide tile of the prefill GEMM leaves most CUs idle
+    // (one work item per 128 tokens); 128 x 128 tiles give twice the items or more
+    const bool wide = c.n_routed > 256 && gemm_mfma2_supported(&s, 1);
+    e = wide ? launch_gemm_mfma2(&s, 1, EPI_STORE, true, st)
+             : launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
   } else {
     e = launch_gate_logits_gemv(c, T, x, w_gate, logits, st);
   }

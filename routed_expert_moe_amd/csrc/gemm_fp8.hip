@@ -391,23 +391,46 @@ int cu_count() {
   return n;
 }
 
-// ---- activation quantisation: one wavefront per 128-column run of a row
+// ---- activation quantisation: 16 lanes per 128-column run (8 values each, one
+// 16-byte load), the run's max over the 16-lane row by DPP moves
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));   // mirror within 8
+  v = fmaxf(v, dpp_f32<0x140>(v));   // mirror within 16
+  return v;
+}
+
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t *__restrict__ x, int64_t runs,
                                                         int64_t cols, uint8_t *__restrict__ q,
                                                         float *__restrict__ s) {
-  const int lane = threadIdx.x & 63;
-  const int64_t run = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (run >= runs) return;   // wavefront-uniform
+  const int l16 = threadIdx.x & 15;
+  const int64_t run = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  if (run >= runs) return;   // uniform over the 16 lanes of a run (a DPP row)
   const int64_t nb = cols / 128;
   const int64_t row = run / nb, cb = run - row * nb;
-  const uint32_t two = *reinterpret_cast<const uint32_t *>(x + row * cols + cb * 128 + 2 * lane);
-  const float a = __uint_as_float(two << 16), b = __uint_as_float(two & 0xFFFF0000u);
-  float m = fmaxf(fabsf(a), fabsf(b));
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const int64_t at = row * cols + cb * 128 + 8 * l16;
+  const u32x4_t v = *reinterpret_cast<const u32x4_t *>(x + at);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = row_max16(m);
   const float sc = m > 0.0f ? m / kE4m3Max : 1.0f;
-  const uint32_t pair = e4m3_pair(a / sc, b / sc);
-  *reinterpret_cast<uint16_t *>(q + row * cols + cb * 128 + 2 * lane) = static_cast<uint16_t>(pair);
-  if (lane == 0) s[row * nb + cb] = sc;
+  uint2 o;
+  o.x = e4m3_pair(f[0] / sc, f[1] / sc) | (e4m3_pair(f[2] / sc, f[3] / sc) << 16);
+  o.y = e4m3_pair(f[4] / sc, f[5] / sc) | (e4m3_pair(f[6] / sc, f[7] / sc) << 16);
+  *reinterpret_cast<uint2 *>(q + at) = o;
+  if (l16 == 0) s[row * nb + cb] = sc;
 }
 
 }  // namespace
@@ -442,7 +465,7 @@ hipError_t launch_quant_act(const void *x, int64_t rows, int64_t cols, uint8_t *
                             hipStream_t st) {
   const int64_t runs = rows * (cols / 128);
   if (runs == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((runs + 3) / 4)), block(256);
+  const dim3 grid(static_cast<unsigned>((runs + 15) / 16)), block(256);
   hipLaunchKernelGGL(quant_act_kernel, grid, block, 0, st, static_cast<const uint16_t *>(x), runs,
                      cols, q, s);
   return hipGetLastError();
