@@ -54,3 +54,35 @@ def bias_update(bias: np.ndarray, loads: np.ndarray, n_tokens: int, top_k: int,
         elif scaled < total:
             b[e] = b[e] + g
     return b
+
+
+def sequence_balance_loss(logits: np.ndarray, idx: np.ndarray, score: str, alpha: float,
+                          seq_len: int) -> np.ndarray:
+    """Sequence-wise balance loss, one value per sequence of seq_len tokens.
+
+    DeepSeek-V3 notes page, "V3 improvement 2" (the paper's eqs. 17-20):
+        L_Bal = alpha * sum_i f_i * P_i,
+        f_i = E / (K * T_s) * #{t : i is among token t's chosen experts},
+        s'_{i,t} = s_{i,t} / sum_j s_{j,t},   P_i = (1/T_s) * sum_t s'_{i,t},
+    over the T_s = seq_len tokens of a sequence.  s is the unbiased score of
+    the gate (sigmoid of the logit, or the softmax probability); the chosen
+    experts are the routing the layer used (idx).  float64 throughout.
+    """
+    l = np.asarray(logits, np.float64)
+    T, E = l.shape
+    K = idx.shape[1]
+    assert T % seq_len == 0, (T, seq_len)
+    if score == "sigmoid":
+        s = 1.0 / (1.0 + np.exp(-l))
+    else:
+        z = np.exp(l - l.max(axis=1, keepdims=True))
+        s = z / z.sum(axis=1, keepdims=True)
+    sn = s / s.sum(axis=1, keepdims=True)
+    out = np.empty(T // seq_len)
+    for q in range(T // seq_len):
+        rows = slice(q * seq_len, (q + 1) * seq_len)
+        counts = expert_loads(idx[rows], E).astype(np.float64)
+        f = counts * E / (K * seq_len)
+        P = sn[rows].mean(axis=0)
+        out[q] = alpha * float(np.dot(f, P))
+    return out

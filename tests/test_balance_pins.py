@@ -103,3 +103,49 @@ def test_repeated_updates_balance_the_experts():
         loads, _ = imbalance(bias)
     _, end = imbalance(bias)
     assert end < 0.5 * start and end < 1.6
+
+
+def test_golden_sequence_balance_loss():
+    g = _fixture("balance_loss_worked_example.txt")
+    logits = np.array([[float(v) for v in g["logit0"].split()], [float(v) for v in g["logit1"].split()]])
+    a = float(g["alpha"])
+    split = balance.sequence_balance_loss(logits, np.array([[0], [1]]), "softmax", a, 2)
+    same = balance.sequence_balance_loss(logits, np.array([[0], [0]]), "softmax", a, 2)
+    assert np.isclose(split[0], float(g["expect_split"]), rtol=1e-12)
+    assert np.isclose(same[0], float(g["expect_same"]), rtol=1e-12)
+
+
+def test_balance_loss_closed_forms():
+    # equal scores and perfectly balanced routing: f_i = 1, P_i = 1/E -> L = alpha
+    E, K, T = 16, 4, 64
+    idx = (np.arange(T * K) % E).reshape(T, K)
+    for score in ("sigmoid", "softmax"):
+        loss = balance.sequence_balance_loss(np.zeros((T, E)), idx, score, 0.01, T)
+        assert np.isclose(loss[0], 0.01, rtol=1e-12)
+    # every token on the same K experts with equal scores: f = E/K on those, L = alpha * E/K * K/E... = alpha
+    # (sum of P over the chosen experts is K/E); a skewed score profile matched to the routing costs more
+    idx1 = np.tile(np.arange(K), (T, 1))
+    assert np.isclose(balance.sequence_balance_loss(np.zeros((T, E)), idx1, "softmax", 1.0, T)[0], 1.0)
+    skew = np.zeros((T, E))
+    skew[:, :K] = 2.0
+    assert balance.sequence_balance_loss(skew, idx1, "softmax", 1.0, T)[0] > 1.5
+
+
+def test_balance_loss_sequences_are_independent_and_relabeling_invariant():
+    rng = np.random.default_rng(8)
+    E, K, S = 12, 3, 40
+    l = rng.standard_normal((2 * S, E))
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(2 * S)])
+    both = balance.sequence_balance_loss(l, idx, "sigmoid", 0.1, S)
+    first = balance.sequence_balance_loss(l[:S], idx[:S], "sigmoid", 0.1, S)
+    second = balance.sequence_balance_loss(l[S:], idx[S:], "sigmoid", 0.1, S)
+    assert np.allclose(both, [first[0], second[0]], rtol=1e-13)
+    perm = rng.permutation(E)
+    inv = np.argsort(perm)
+    relabel = balance.sequence_balance_loss(l[:, perm], inv[idx], "sigmoid", 0.1, 2 * S)
+    assert np.isclose(relabel[0], balance.sequence_balance_loss(l, idx, "sigmoid", 0.1, 2 * S)[0],
+                      rtol=1e-12)
+    # the score is normalised per token: adding a constant to a token's softmax logits changes nothing
+    l2 = l + rng.standard_normal((2 * S, 1))
+    assert np.allclose(balance.sequence_balance_loss(l2, idx, "softmax", 0.1, S),
+                       balance.sequence_balance_loss(l, idx, "softmax", 0.1, S), rtol=1e-12)
