@@ -205,6 +205,29 @@ def time_bias_update(p: Pass, shape, calls: int = 200):
             "bound": "launch latency", "bytes_per_call": shape.n_routed * 12}
 
 
+def time_balance_loss(p: Pass, shape, calls: int = 20):
+    """The sequence-wise balance loss of the last timed batch (two sequences of T/2).
+
+    A training-time reduction over the [T, E] logits and the routing; it reads
+    T*E*4 + T*K*4 bytes, so HBM is its ceiling."""
+    import torch
+    B = p.B
+    loss = torch.empty(2, dtype=torch.float32, device="cuda")
+    B.moe_balance_loss(p.cfg, p.T, p.T // 2, p.logits, p.idx, 1e-4, loss)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(calls):
+        B.moe_balance_loss(p.cfg, p.T, p.T // 2, p.logits, p.idx, 1e-4, loss)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / calls * 1e3
+    nbytes = p.T * shape.n_routed * 4 + p.T * shape.top_k * 4
+    return {"what": "moe_balance_loss (sequence-wise balance loss), 2 sequences of T/2 tokens",
+            "us_per_call": us, "bytes_per_call": nbytes, "gbs": nbytes / us / 1e3}
+
+
 def cpu_baseline(layer, n_tokens: int):
     """The float64 oracle on the first n_tokens tokens of the same workload, on host cores."""
     import numpy as np
@@ -283,6 +306,7 @@ def main():
         "wall_s": wall,
     }
     res["bias_update"] = time_bias_update(p, shape)
+    res["balance_loss"] = time_balance_loss(p, shape)
     del p
     torch.cuda.empty_cache()
 

@@ -241,6 +241,19 @@ moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const mo
 moe_status moe_bias_update(const moe_config *cfg, int64_t T, const moe_routing *r, float gamma,
                            float *bias, void *stream);
 
+/* Sequence-wise balance loss (DeepSeek-V3 notes page, "V3 improvement 2", the
+ * paper's eqs. 17-20), one value per sequence of seq_len consecutive tokens:
+ *   loss[q] = alpha * sum_i f_i * P_i,
+ *   f_i = n_routed / (top_k * seq_len) * (tokens of the sequence with i in topk_idx),
+ *   P_i = (1/seq_len) * sum_t s_{i,t} / sum_j s_{j,t},
+ * s = sigmoid(logit) for MOE_SCORE_SIGMOID, the softmax probability for
+ * MOE_SCORE_SOFTMAX (the unbiased score; no bias enters).  Sums of s' run in
+ * fp64; the result is rounded once to fp32 and is the same on every run.
+ *   logits [T, E] fp32 (moe_gate's logits), topk_idx [T, K] int32,
+ *   loss [T / seq_len] fp32 out;  T % seq_len == 0, seq_len >= 1, alpha finite. */
+moe_status moe_balance_loss(const moe_config *cfg, int64_t T, int32_t seq_len, const float *logits,
+                            const int32_t *topk_idx, float alpha, float *loss, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,7 +63,7 @@ class moe_routing(ctypes.Structure):
 EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspace_size",
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update",
-            "moe_quant_act")
+            "moe_quant_act", "moe_balance_loss")
 
 _lib = None
 
@@ -95,6 +95,7 @@ def lib():
         "moe_forward": [cfgp, I64, P, ctypes.POINTER(moe_weights), P, P, P, P, SZ, P],
         "moe_bias_update": [cfgp, I64, ctypes.POINTER(moe_routing), ctypes.c_float, P, P],
         "moe_quant_act": [cfgp, I64, P, ctypes.POINTER(moe_routing), P],
+        "moe_balance_loss": [cfgp, I64, ctypes.c_int32, P, P, ctypes.c_float, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -243,6 +244,12 @@ def moe_combine(cfg: moe_config, T: int, u, z, y_pairs, routing: Routing, topk_w
 
 def moe_quant_act(cfg: moe_config, T: int, x, routing: Routing, stream=None) -> None:
     _check(lib().moe_quant_act(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(routing.struct), _stream(stream)))
+
+
+def moe_balance_loss(cfg: moe_config, T: int, seq_len: int, logits, topk_idx, alpha: float, loss,
+                     stream=None) -> None:
+    _check(lib().moe_balance_loss(ctypes.byref(cfg), T, int(seq_len), _ptr(logits), _ptr(topk_idx),
+                                  float(alpha), _ptr(loss), _stream(stream)))
 
 
 def moe_bias_update(cfg: moe_config, T: int, routing: Routing, gamma: float, bias, stream=None) -> None:

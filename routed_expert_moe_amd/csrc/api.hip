@@ -549,6 +549,25 @@ moe_status moe_quant_act(const moe_config *cfg, int64_t T, const void *x, const 
   return ok();
 }
 
+moe_status moe_balance_loss(const moe_config *cfg, int64_t T, int32_t seq_len, const float *logits,
+                            const int32_t *topk_idx, float alpha, float *loss, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  if (seq_len < 1) return fail(MOE_ERR_INVALID_ARG, "seq_len must be >= 1");
+  if (T % seq_len != 0) return fail(MOE_ERR_INVALID_ARG, "T must be a multiple of seq_len");
+  if (!isfinite(alpha)) return fail(MOE_ERR_INVALID_ARG, "alpha must be finite");
+  if (logits == nullptr || topk_idx == nullptr || loss == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "logits, topk_idx and loss must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(topk_idx) |
+       reinterpret_cast<uintptr_t>(loss)) % 4 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "logits, topk_idx and loss must be 4-byte aligned");
+  if (T == 0) return ok();
+  const hipError_t e = launch_balance_loss(*cfg, T, seq_len, logits, topk_idx, alpha, loss,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "balance loss launch");
+  return ok();
+}
+
 moe_status moe_bias_update(const moe_config *cfg, int64_t T, const moe_routing *r, float gamma,
                            float *bias, void *stream) {
   MOE_TRY(check_cfg(cfg));

@@ -128,6 +128,18 @@ def test_bias_update_validates_before_launch():
     assert L.moe_bias_update(ctypes.byref(c), 0, ctypes.byref(r0), 1e-3, fake, None) == B.MOE_OK
 
 
+def test_balance_loss_validates_before_launch():
+    c = _cfg()
+    L = B.lib()
+    fake = 1 << 20
+    assert L.moe_balance_loss(ctypes.byref(c), 64, 0, fake, fake, ctypes.c_float(1.0), fake, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_loss(ctypes.byref(c), 64, 48, fake, fake, ctypes.c_float(1.0), fake, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_loss(ctypes.byref(c), 64, 32, fake, fake, ctypes.c_float(float("nan")), fake, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_loss(ctypes.byref(c), 64, 32, None, fake, ctypes.c_float(1.0), fake, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_loss(ctypes.byref(c), 64, 32, fake, fake, ctypes.c_float(1.0), fake + 2, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_loss(ctypes.byref(c), 0, 32, fake, fake, ctypes.c_float(1.0), fake, None) == B.MOE_OK
+
+
 def test_T_zero_is_a_no_op():
     c = _cfg()
     L = B.lib()

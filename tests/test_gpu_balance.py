@@ -124,3 +124,49 @@ def test_repeated_balancing_steps():
         assert np.array_equal(_bits(bias), ref.view(np.uint32))
         spread.append(loads.max() - loads.min())
     assert spread[-1] < spread[0]
+
+
+@pytest.mark.parametrize("E,K,T,seq_len,score", [
+    (16, 4, 64, 64, "sigmoid"), (16, 2, 300, 100, "softmax"), (256, 8, 8192, 4096, "sigmoid"),
+    (160, 6, 4096, 1, "softmax"), (512, 32, 96, 32, "sigmoid"), (37, 3, 50, 25, "sigmoid")])
+def test_balance_loss_matches_oracle(E, K, T, seq_len, score):
+    """Seeded logits and routings given to both sides."""
+    say(f"[moe_balance_loss] E={E} K={K} T={T} seq_len={seq_len} {score}")
+    g = torch.Generator().manual_seed(E * 1000 + T)
+    logits = torch.randn(T, E, generator=g) * 2.0
+    idx = torch.stack([torch.randperm(E, generator=g)[:K] for _ in range(T)]).to(torch.int32)
+    shape = LayerShape(name="bl", T=T, dim=128, n_routed=E, n_groups=1, topk_groups=1, top_k=K,
+                       n_shared=0, inter_dim=128, score=score, route_scale=1.0, act="f32", weight="f32")
+    cfg = B.config_of(shape)
+    loss = torch.empty(T // seq_len, dtype=torch.float32, device="cuda")
+    B.moe_balance_loss(cfg, T, seq_len, logits.cuda(), idx.cuda(), 1e-3, loss)
+    torch.cuda.synchronize()
+    want = balance.sequence_balance_loss(logits.numpy().astype(np.float64), idx.numpy(), score, 1e-3, seq_len)
+    got = loss.cpu().numpy().astype(np.float64)
+    assert np.allclose(got, want, rtol=2e-6, atol=0)
+    loss2 = torch.empty_like(loss)
+    B.moe_balance_loss(cfg, T, seq_len, logits.cuda(), idx.cuda(), 1e-3, loss2)
+    torch.cuda.synchronize()
+    assert torch.equal(loss, loss2)
+
+
+def test_balance_loss_on_the_v3_gate():
+    """The V3 prefill batch: the oracle forms its own float64 logits from x and W_g and
+    uses the GPU's (certified) routing for the indicator."""
+    import oracle
+    from oracle_bridge import to_f64
+    shape = configs.V3_PREFILL_BF16
+    say("[moe_balance_loss] v3 prefill gate")
+    x, w_gate, bias = synth.make_gate_inputs(shape, device="cuda")
+    cfg = B.config_of(shape)
+    T, E, K = shape.T, shape.n_routed, shape.top_k
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    B.moe_gate(cfg, T, x, w_gate, bias, logits, idx, w)
+    loss = torch.empty(2, dtype=torch.float32, device="cuda")
+    B.moe_balance_loss(cfg, T, T // 2, logits, idx, 1e-4, loss)
+    torch.cuda.synchronize()
+    l64 = oracle.gate_logits(to_f64(x), to_f64(w_gate))
+    want = balance.sequence_balance_loss(l64, idx.cpu().numpy(), "sigmoid", 1e-4, T // 2)
+    assert np.allclose(loss.cpu().numpy().astype(np.float64), want, rtol=1e-5, atol=0)
