@@ -4,12 +4,13 @@
 // At decode the weights are nearly all of the bytes, so the kernel is built to
 // keep HBM busy:
 //  * persistent grid (as many workgroups as fit on the CUs at once); every wavefront takes work
-//    items (tile, pair of 16-row weight groups) from one list that holds only
+//    items (tile, NG 16-row weight groups) from one list that holds only
 //    the tiles in use, so no workgroup is launched for an untouched expert;
-//  * each wavefront streams its two groups over the whole K, loading 128-wide
-//    K blocks k+1 and k+2 while it multiplies block k (with 12-16 wavefronts
-//    per CU about 100 KiB of weights stay in flight per CU, which covers the
-//    several-microsecond HBM latency under full load);
+//  * each wavefront streams its NG groups over the whole K, loading the next
+//    one or two 128-wide K blocks while it multiplies block k (NG and the
+//    buffer count are set per kernel below so that 64-128 KiB of weights stay
+//    in flight per CU, which covers the several-microsecond HBM latency under
+//    full load);
 //  * within a 128-wide K block, lane (row n = lane%16, quarter q = lane/16)
 //    owns 32 K positions of its weight row, chosen so that the four lanes of a
 //    row read one contiguous 64-byte run per load; the A fragments use the
@@ -19,8 +20,8 @@
 // each 128-wide K block is accumulated separately and added times its fp32
 // block scale: acc += s[n/128][k/128] * partial.
 //
-// SwiGLU items pair 16 gate rows with the 16 matching up rows; plain items two
-// consecutive 16-row groups.  Consecutive items share their tile's A rows, and
+// SwiGLU items pair NG/2 16-row gate groups with the matching up groups; plain
+// items take NG consecutive 16-row groups.  Consecutive items share their tile's A rows, and
 // the four wavefronts of a workgroup take consecutive items.
 #include "common.hpp"
 
@@ -29,11 +30,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// 16-row weight groups per work item and K-block buffers per wavefront.  The
+// fp8 kernels are limited by the weight bytes each wavefront keeps in flight,
+// so they take as many groups as the registers allow: gate/up (K = model dim,
+// long) 8 groups double-buffered at one wavefront per SIMD, down 4 groups
+// triple-buffered at two.
+template <bool FP8, bool UP> constexpr int kGroups = !FP8 ? 2 : UP ? 8 : 4;
+template <bool FP8, bool UP> constexpr int kBufs = FP8 && UP ? 2 : 3;
+int groups_per_item(bool fp8, bool up) { return !fp8 ? 2 : up ? 8 : 4; }
 
 struct Work {
   Segment seg[2];
   int nseg;
-  int ngp[2];                             // 16-row group pairs per tile
+  int ngp[2];                             // work items per tile
 };
 
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
@@ -55,14 +64,16 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // operands of one 128-wide K block for this lane
-template <bool FP8>
+template <bool FP8, bool UP>
 struct KBlock {
   u32x4_t a[4];                  // A: 4 x 8 bf16
-  u32x4_t w[2][FP8 ? 2 : 4];     // per group: 32 fp8 (2 x 16 B) or 32 bf16 (4 x 16 B)
+  u32x4_t w[kGroups<FP8, UP>][FP8 ? 2 : 4];     // per group: 32 fp8 (2 x 16 B) or 32 bf16 (4 x 16 B)
 };
 
 template <int EPI, bool FP8, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
+  constexpr bool UP = EPI == EPI_SWIGLU;
+  constexpr int NG = kGroups<FP8, UP>, HG = NG / 2;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int l16 = lane & 15, q = lane >> 4;
@@ -98,18 +109,18 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
         arow = A + static_cast<int64_t>(grow) * sg.lda;
       }
     }
-    // weight rows of this lane's two groups, and whether each group exists
-    int base[2], wrow[2];
-    bool gvalid[2], wvalid[2];
+    // weight rows of this lane's groups, and whether each group exists
+    int base[NG], wrow[NG];
+    bool gvalid[NG], wvalid[NG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
       if (EPI == EPI_SWIGLU) {
-        const int col0 = gp * 16;
-        base[g] = g == 0 ? col0 : half_n + col0;
+        const int col0 = gp * 16 * HG + (g % HG) * 16;
+        base[g] = g < HG ? col0 : half_n + col0;
         gvalid[g] = col0 < half_n;
         wvalid[g] = col0 + l16 < half_n;
       } else {
-        base[g] = gp * 32 + g * 16;
+        base[g] = gp * 16 * NG + g * 16;
         gvalid[g] = base[g] < sg.n;
         wvalid[g] = base[g] + l16 < sg.n;
       }
@@ -125,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
     auto kpos = [&](int kb, int i) -> int {
       return FP8 ? kb * 128 + (i >> 1) * 64 + 16 * q + (i & 1) * 8 : kb * 128 + 32 * i + 8 * q;
     };
-    auto load_kb = [&](int kb, KBlock<FP8> &d) {
+    auto load_kb = [&](int kb, KBlock<FP8, UP> &d) {
       const bool kin = kb < kblocks;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -134,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
                                                    : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         if (FP8) {
           const uint8_t *wp = static_cast<const uint8_t *>(sg.b) + eoff + static_cast<int64_t>(wrow[g]) * K;
           const bool ok = wvalid[g] && kin;
@@ -152,16 +163,16 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
       }
     };
 
-    f32x4_t acc[2];
+    f32x4_t acc[NG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute_kb = [&](int kb, const KBlock<FP8> &d) {
+    auto compute_kb = [&](int kb, const KBlock<FP8, UP> &d) {
       bf16x8_t af[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8_t, d.a[i]);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         if (FP8) {
           const bf16x8_t b0 = fp8x8_to_bf16x8(d.w[g][0][0], d.w[g][0][1]);
           const bf16x8_t b1 = fp8x8_to_bf16x8(d.w[g][0][2], d.w[g][0][3]);
@@ -184,19 +195,32 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
       }
     };
 
-    // three K-block buffers: blocks kb+1 and kb+2 load while kb multiplies
-    KBlock<FP8> buf[3];
-    load_kb(0, buf[0]);
-    load_kb(1, buf[1]);
-    for (int kb = 0; kb < kblocks; kb += 3) {
-      load_kb(kb + 2, buf[2]);
-      compute_kb(kb, buf[0]);
-      if (kb + 1 >= kblocks) break;
-      load_kb(kb + 3, buf[0]);
-      compute_kb(kb + 1, buf[1]);
-      if (kb + 2 >= kblocks) break;
-      load_kb(kb + 4, buf[1]);
-      compute_kb(kb + 2, buf[2]);
+    // K-block buffers: with two, block kb+1 loads while kb multiplies; with
+    // three, blocks kb+1 and kb+2
+    if constexpr (kBufs<FP8, UP> == 2) {
+      KBlock<FP8, UP> buf[2];
+      load_kb(0, buf[0]);
+      for (int kb = 0; kb < kblocks; kb += 2) {
+        load_kb(kb + 1, buf[1]);
+        compute_kb(kb, buf[0]);
+        if (kb + 1 >= kblocks) break;
+        load_kb(kb + 2, buf[0]);
+        compute_kb(kb + 1, buf[1]);
+      }
+    } else {
+      KBlock<FP8, UP> buf[3];
+      load_kb(0, buf[0]);
+      load_kb(1, buf[1]);
+      for (int kb = 0; kb < kblocks; kb += 3) {
+        load_kb(kb + 2, buf[2]);
+        compute_kb(kb, buf[0]);
+        if (kb + 1 >= kblocks) break;
+        load_kb(kb + 3, buf[0]);
+        compute_kb(kb + 1, buf[1]);
+        if (kb + 2 >= kblocks) break;
+        load_kb(kb + 4, buf[1]);
+        compute_kb(kb + 2, buf[2]);
+      }
     }
 
     // epilogue: lane holds column l16 of the group (a weight row), tile rows 4q + r
@@ -205,14 +229,17 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
       const int grow = row0 + 4 * q + r;
       if (dense && grow >= sg.a_rows) continue;
       if (EPI == EPI_SWIGLU) {
-        const int col = gp * 16 + l16;
-        if (col < half_n) {
-          const float h = silu_mul(acc[0][r], acc[1][r]);
-          static_cast<uint16_t *>(sg.c)[static_cast<int64_t>(grow) * sg.ldc + col] = f32_to_bf16_bits(h);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const int col = gp * 16 * HG + hg * 16 + l16;
+          if (col < half_n) {
+            const float h = silu_mul(acc[hg][r], acc[hg + HG][r]);
+            static_cast<uint16_t *>(sg.c)[static_cast<int64_t>(grow) * sg.ldc + col] = f32_to_bf16_bits(h);
+          }
         }
       } else {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < NG; ++g) {
           if (!wvalid[g]) continue;
           const int64_t o = static_cast<int64_t>(grow) * sg.ldc + wrow[g];
           if (OUT_F32)
@@ -241,11 +268,12 @@ int cu_count() {
 hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool w_fp8,
                               bool out_f32, hipStream_t st) {
   Work wk{};
+  const int NG = groups_per_item(w_fp8, epi == EPI_SWIGLU), HG = NG / 2;
   wk.nseg = nseg;
   int64_t cap = 0;
   for (int s = 0; s < nseg; ++s) {
     wk.seg[s] = segs[s];
-    wk.ngp[s] = epi == EPI_SWIGLU ? (segs[s].n / 2 + 15) / 16 : (segs[s].n + 31) / 32;
+    wk.ngp[s] = epi == EPI_SWIGLU ? (segs[s].n / 2 + 16 * HG - 1) / (16 * HG) : (segs[s].n + 16 * NG - 1) / (16 * NG);
     cap += static_cast<int64_t>(segs[s].n_tiles_host) * wk.ngp[s];
   }
   if (cap == 0) return hipSuccess;
