@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-# Measured HBM traffic per launch of the two roofline kernels: rocprofv3 --pmc
+# Measured HBM traffic per launch of the roofline kernels: rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the layer's
 # launches), scaled by what the same counters read for a 1 GiB device copy
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  The commands and per-dispatch values
@@ -40,13 +40,17 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_mfma2.hip", "common.hpp"),
-                   "sha256": "b292c827d020aad8d2692f218713c8f6a735b6e8c472cf185e27a2196add3ce8",
-                   "fetch_kib": 8671144, "write_kib": 362496,
+                   "sha256": "6bf092fe7fc2460195aa99bb5c40c866cd37d3ca8d0941d8e66f26abbf8a551b",
+                   "fetch_kib": 8563229, "write_kib": 362496,
                    "profile": "profiles/gemm_mfma2_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
-                  "sha256": "3a9c66c4dbac940d8bbd188f9a574f101f7f5753765fe16a0ae3765b90789cfb",
-                  "fetch_kib": 849218, "write_kib": 4272,
+                  "sha256": "4a481e0e556252bf420a7159ff1d6888326a61fd4c1468ad53f555c8d85b3810",
+                  "fetch_kib": 847323, "write_kib": 3744,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
+    "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
+                "sha256": "0a5337e341a86f335144b52c53da740ae474826da37057f71ce0f3873ca99f95",
+                "fetch_kib": 8186954, "write_kib": 193260,
+                "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
 }
 
 
@@ -154,11 +158,18 @@ def work_figures(layer, counts):
     sw13 = 2 * S * I * D * wb + (2 * S * I // 128) * (D // 128) * 4 * (s.weight == "fp8") if S else 0
     sw2 = D * S * I * wb + (D // 128) * (S * I // 128) * 4 * (s.weight == "fp8") if S else 0
     flops_up = 2 * P * 2 * I * D + 2 * T * 2 * S * I * D
-    bytes_up = touched * w13_e + sw13 + T * D * ab + P * I * ab + T * S * I * ab
+    # W8A8: gate/up reads x and writes h as e4m3 codes plus one fp32 scale per 128
+    qb = 1 + 4 / 128 if s.act_quant else ab
+    bytes_up = touched * w13_e + sw13 + T * D * qb + P * I * qb + T * S * I * qb
     flops_layer = 2 * T * E * D + 2 * P * 3 * I * D + 2 * T * 3 * S * I * D
     bytes_layer = touched * (w13_e + w2_e) + sw13 + sw2 + E * D * ab + 2 * T * D * ab
     return dict(touched=touched, flops_up=flops_up, bytes_up=bytes_up, flops_layer=flops_layer,
                 bytes_layer=bytes_layer)
+
+
+def progress(msg: str) -> None:
+    """One line per phase on stderr (stdout carries only the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def time_pass(p: Pass, steps: int, warmup: int):
@@ -213,13 +224,15 @@ def time_balance_loss(p: Pass, shape, calls: int = 20):
     import torch
     B = p.B
     loss = torch.empty(2, dtype=torch.float32, device="cuda")
-    B.moe_balance_loss(p.cfg, p.T, p.T // 2, p.logits, p.idx, 1e-4, loss)
+    ws = torch.empty(max(B.moe_balance_loss_workspace_size(p.cfg, p.T, p.T // 2), 256), dtype=torch.uint8,
+                     device="cuda")
+    B.moe_balance_loss(p.cfg, p.T, p.T // 2, p.logits, p.idx, 1e-4, loss, workspace=ws)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record()
     for _ in range(calls):
-        B.moe_balance_loss(p.cfg, p.T, p.T // 2, p.logits, p.idx, 1e-4, loss)
+        B.moe_balance_loss(p.cfg, p.T, p.T // 2, p.logits, p.idx, 1e-4, loss, workspace=ws)
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / calls * 1e3
@@ -281,7 +294,9 @@ def main():
 
     # ---- prefill: the headline workload
     shape = configs.V3_PREFILL_BF16
+    progress(f"building {shape.name}")
     layer = synth.make_layer(shape, device="cuda")
+    progress(f"timing {shape.name}")
     p = Pass(layer)
     total_ms, up_ms, wall = time_pass(p, args.steps, args.warmup)
     counts = p.r.counts.cpu().numpy()
@@ -312,7 +327,9 @@ def main():
 
     # ---- the same prefill batch in FP8 W8A8 (fp8 weights, activations quantised 1x128)
     wshape = configs.V3_PREFILL_W8A8
+    progress(f"building {wshape.name}")
     wlayer = synth.make_layer(wshape, device="cuda")
+    progress(f"timing {wshape.name}")
     wp = Pass(wlayer)
     wtotal_ms, wup_ms, _ = time_pass(wp, args.steps, args.warmup)
     wfig = work_figures(wlayer, wp.r.counts.cpu().numpy())
@@ -324,7 +341,7 @@ def main():
         "experts_touched": wfig["touched"],
         "layer_tflops": wfig["flops_layer"] / (wms / 1e3) / 1e12,
         "layer_mfma_frac_fp8": wfig["flops_layer"] / (wms / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
-        "roofline": roofline(wfig["flops_up"], wfig["bytes_up"], wup_ms, None,
+        "roofline": roofline(wfig["flops_up"], wfig["bytes_up"], wup_ms, measured_traffic("w8a8_up"),
                              "moe_expert_up (fp8 x fp8 grouped GEMM + SwiGLU + h quantisation, gemm_fp8_kernel)",
                              PEAK_FP8_TFLOPS),
     }
@@ -333,7 +350,9 @@ def main():
 
     # ---- decode: 8 tokens, fp8 expert weights
     dshape = configs.V3_DECODE_FP8
+    progress(f"building {dshape.name}")
     dlayer = synth.make_layer(dshape, device="cuda")
+    progress(f"timing {dshape.name}")
     dp = Pass(dlayer)
     dsteps = args.decode_steps or 10 * args.steps
     dtotal_ms, dup_ms, _ = time_pass(dp, dsteps, max(args.warmup, 3))
@@ -350,6 +369,7 @@ def main():
     }
     del dp, dlayer
     if not args.no_cpu_baseline:
+        progress("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(layer, args.cpu_tokens)
     print(json.dumps(res), flush=True)
 

@@ -248,11 +248,22 @@ moe_status moe_bias_update(const moe_config *cfg, int64_t T, const moe_routing *
  *   P_i = (1/seq_len) * sum_t s_{i,t} / sum_j s_{j,t},
  * s = sigmoid(logit) for MOE_SCORE_SIGMOID, the softmax probability for
  * MOE_SCORE_SOFTMAX (the unbiased score; no bias enters).  Sums of s' run in
- * fp64; the result is rounded once to fp32 and is the same on every run.
+ * fp64 in a fixed order; the result is rounded once to fp32 and is the same on
+ * every run.
  *   logits [T, E] fp32 (moe_gate's logits), topk_idx [T, K] int32,
- *   loss [T / seq_len] fp32 out;  T % seq_len == 0, seq_len >= 1, alpha finite. */
+ *   workspace: device memory of >= moe_balance_loss_workspace_size bytes,
+ *     256-byte aligned, owned by the caller; it holds per-chunk partial sums
+ *     between the two launches of one call and needs no initial contents;
+ *   loss [T / seq_len] fp32 out;  T % seq_len == 0, seq_len >= 1, alpha finite.
+ * A workspace that is too small returns MOE_ERR_WORKSPACE before any launch. */
 moe_status moe_balance_loss(const moe_config *cfg, int64_t T, int32_t seq_len, const float *logits,
-                            const int32_t *topk_idx, float alpha, float *loss, void *stream);
+                            const int32_t *topk_idx, float alpha, void *workspace,
+                            size_t workspace_bytes, float *loss, void *stream);
+
+/* Bytes of workspace moe_balance_loss needs for (cfg, T, seq_len): about
+ * 12 * n_routed * T / 64 (0 when T == 0).  Host only. */
+moe_status moe_balance_loss_workspace_size(const moe_config *cfg, int64_t T, int32_t seq_len,
+                                           size_t *bytes);
 
 #ifdef __cplusplus
 }

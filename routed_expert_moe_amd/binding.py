@@ -63,7 +63,7 @@ class moe_routing(ctypes.Structure):
 EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspace_size",
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update",
-            "moe_quant_act", "moe_balance_loss")
+            "moe_quant_act", "moe_balance_loss", "moe_balance_loss_workspace_size")
 
 _lib = None
 
@@ -95,7 +95,8 @@ def lib():
         "moe_forward": [cfgp, I64, P, ctypes.POINTER(moe_weights), P, P, P, P, SZ, P],
         "moe_bias_update": [cfgp, I64, ctypes.POINTER(moe_routing), ctypes.c_float, P, P],
         "moe_quant_act": [cfgp, I64, P, ctypes.POINTER(moe_routing), P],
-        "moe_balance_loss": [cfgp, I64, ctypes.c_int32, P, P, ctypes.c_float, P, P],
+        "moe_balance_loss": [cfgp, I64, ctypes.c_int32, P, P, ctypes.c_float, P, ctypes.c_size_t, P, P],
+        "moe_balance_loss_workspace_size": [cfgp, I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -120,6 +121,15 @@ def _ptr(t: Optional[torch.Tensor]):
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
     return t.data_ptr()
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _device_bytes(n: int, like: torch.Tensor) -> torch.Tensor:
+    """A device byte buffer of at least n bytes on like's device (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=like.device)
 
 
 def _stream(stream) -> Optional[int]:
@@ -246,10 +256,20 @@ def moe_quant_act(cfg: moe_config, T: int, x, routing: Routing, stream=None) -> 
     _check(lib().moe_quant_act(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(routing.struct), _stream(stream)))
 
 
+def moe_balance_loss_workspace_size(cfg: moe_config, T: int, seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_balance_loss_workspace_size(ctypes.byref(cfg), T, int(seq_len), ctypes.byref(n)))
+    return n.value
+
+
 def moe_balance_loss(cfg: moe_config, T: int, seq_len: int, logits, topk_idx, alpha: float, loss,
-                     stream=None) -> None:
+                     stream=None, workspace=None) -> None:
+    """workspace: a device buffer of >= moe_balance_loss_workspace_size bytes (allocated here if None)."""
+    if workspace is None:
+        workspace = _device_bytes(moe_balance_loss_workspace_size(cfg, T, seq_len), logits)
     _check(lib().moe_balance_loss(ctypes.byref(cfg), T, int(seq_len), _ptr(logits), _ptr(topk_idx),
-                                  float(alpha), _ptr(loss), _stream(stream)))
+                                  float(alpha), _ptr(workspace), _nbytes(workspace), _ptr(loss),
+                                  _stream(stream)))
 
 
 def moe_bias_update(cfg: moe_config, T: int, routing: Routing, gamma: float, bias, stream=None) -> None:

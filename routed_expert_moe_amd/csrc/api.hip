@@ -549,12 +549,26 @@ moe_status moe_quant_act(const moe_config *cfg, int64_t T, const void *x, const 
   return ok();
 }
 
-moe_status moe_balance_loss(const moe_config *cfg, int64_t T, int32_t seq_len, const float *logits,
-                            const int32_t *topk_idx, float alpha, float *loss, void *stream) {
+static moe_status check_balance(const moe_config *cfg, int64_t T, int32_t seq_len) {
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_T(*cfg, T));
   if (seq_len < 1) return fail(MOE_ERR_INVALID_ARG, "seq_len must be >= 1");
   if (T % seq_len != 0) return fail(MOE_ERR_INVALID_ARG, "T must be a multiple of seq_len");
+  return MOE_OK;
+}
+
+moe_status moe_balance_loss_workspace_size(const moe_config *cfg, int64_t T, int32_t seq_len,
+                                           size_t *bytes) {
+  MOE_TRY(check_balance(cfg, T, seq_len));
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = T == 0 ? 0 : balance_loss_workspace_bytes(*cfg, T, seq_len);
+  return ok();
+}
+
+moe_status moe_balance_loss(const moe_config *cfg, int64_t T, int32_t seq_len, const float *logits,
+                            const int32_t *topk_idx, float alpha, void *workspace,
+                            size_t workspace_bytes, float *loss, void *stream) {
+  MOE_TRY(check_balance(cfg, T, seq_len));
   if (!isfinite(alpha)) return fail(MOE_ERR_INVALID_ARG, "alpha must be finite");
   if (logits == nullptr || topk_idx == nullptr || loss == nullptr)
     return fail(MOE_ERR_INVALID_ARG, "logits, topk_idx and loss must be non-NULL");
@@ -562,7 +576,13 @@ moe_status moe_balance_loss(const moe_config *cfg, int64_t T, int32_t seq_len, c
        reinterpret_cast<uintptr_t>(loss)) % 4 != 0)
     return fail(MOE_ERR_INVALID_ARG, "logits, topk_idx and loss must be 4-byte aligned");
   if (T == 0) return ok();
-  const hipError_t e = launch_balance_loss(*cfg, T, seq_len, logits, topk_idx, alpha, loss,
+  const size_t need = balance_loss_workspace_bytes(*cfg, T, seq_len);
+  if (workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(MOE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "balance-loss workspace too small: %zu < %zu", workspace_bytes, need);
+  const hipError_t e = launch_balance_loss(*cfg, T, seq_len, logits, topk_idx, alpha, workspace, loss,
                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "balance loss launch");
   return ok();

@@ -88,8 +88,10 @@ bool gemm_fp8_supported(const Segment *segs, int nseg);
 hipError_t launch_gemm_fp8(const Segment *segs, int nseg, Epilogue epi, hipStream_t st);
 hipError_t launch_quant_act(const void *x, int64_t rows, int64_t cols, uint8_t *q, float *s,
                             hipStream_t st);
+size_t balance_loss_workspace_bytes(const moe_config &cfg, int64_t T, int seq_len);
 hipError_t launch_balance_loss(const moe_config &cfg, int64_t T, int seq_len, const float *logits,
-                               const int32_t *topk_idx, float alpha, float *loss, hipStream_t st);
+                               const int32_t *topk_idx, float alpha, void *workspace, float *loss,
+                               hipStream_t st);
 hipError_t launch_bias_update(const moe_config &cfg, int64_t T, const moe_routing &r, float gamma,
                               float *bias, hipStream_t st);
 hipError_t launch_combine(const moe_config &cfg, int64_t T, const void *u, const void *z,

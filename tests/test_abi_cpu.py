@@ -132,12 +132,23 @@ def test_balance_loss_validates_before_launch():
     c = _cfg()
     L = B.lib()
     fake = 1 << 20
-    assert L.moe_balance_loss(ctypes.byref(c), 64, 0, fake, fake, ctypes.c_float(1.0), fake, None) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_balance_loss(ctypes.byref(c), 64, 48, fake, fake, ctypes.c_float(1.0), fake, None) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_balance_loss(ctypes.byref(c), 64, 32, fake, fake, ctypes.c_float(float("nan")), fake, None) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_balance_loss(ctypes.byref(c), 64, 32, None, fake, ctypes.c_float(1.0), fake, None) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_balance_loss(ctypes.byref(c), 64, 32, fake, fake, ctypes.c_float(1.0), fake + 2, None) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_balance_loss(ctypes.byref(c), 0, 32, fake, fake, ctypes.c_float(1.0), fake, None) == B.MOE_OK
+    one = ctypes.c_float(1.0)
+    ws = B.moe_balance_loss_workspace_size(c, 64, 32)
+    # per-chunk fp64 partials and int32 counts for 2 sequences x 1 chunk x E experts
+    assert ws >= 2 * c.n_routed * 12
+    assert B.moe_balance_loss_workspace_size(c, 0, 32) == 0
+    call = lambda T, sl, lg, a, w, wb, loss: L.moe_balance_loss(ctypes.byref(c), T, sl, lg, fake, a, w, wb, loss, None)
+    assert call(64, 0, fake, one, fake, ws, fake) == B.MOE_ERR_INVALID_ARG       # seq_len < 1
+    assert call(64, 48, fake, one, fake, ws, fake) == B.MOE_ERR_INVALID_ARG      # T % seq_len
+    assert call(64, 32, fake, ctypes.c_float(float("nan")), fake, ws, fake) == B.MOE_ERR_INVALID_ARG
+    assert call(64, 32, None, one, fake, ws, fake) == B.MOE_ERR_INVALID_ARG      # logits NULL
+    assert call(64, 32, fake, one, fake, ws, fake + 2) == B.MOE_ERR_INVALID_ARG  # misaligned loss
+    assert call(64, 32, fake, one, None, ws, fake) == B.MOE_ERR_INVALID_ARG      # no workspace
+    assert call(64, 32, fake, one, fake + 16, ws, fake) == B.MOE_ERR_INVALID_ARG  # misaligned workspace
+    assert call(64, 32, fake, one, fake, ws - 1, fake) == B.MOE_ERR_WORKSPACE     # too small
+    assert call(0, 32, fake, one, None, 0, fake) == B.MOE_OK                      # T == 0: nothing to do
+    with pytest.raises(B.MoeError):
+        B.moe_balance_loss_workspace_size(c, 64, 48)
 
 
 def test_T_zero_is_a_no_op():

@@ -128,7 +128,8 @@ def test_repeated_balancing_steps():
 
 @pytest.mark.parametrize("E,K,T,seq_len,score", [
     (16, 4, 64, 64, "sigmoid"), (16, 2, 300, 100, "softmax"), (256, 8, 8192, 4096, "sigmoid"),
-    (160, 6, 4096, 1, "softmax"), (512, 32, 96, 32, "sigmoid"), (37, 3, 50, 25, "sigmoid")])
+    (160, 6, 4096, 1, "softmax"), (512, 32, 96, 32, "sigmoid"), (37, 3, 50, 25, "sigmoid"),
+    (100, 6, 66, 33, "softmax")])
 def test_balance_loss_matches_oracle(E, K, T, seq_len, score):
     """Seeded logits and routings given to both sides."""
     say(f"[moe_balance_loss] E={E} K={K} T={T} seq_len={seq_len} {score}")
@@ -144,8 +145,11 @@ def test_balance_loss_matches_oracle(E, K, T, seq_len, score):
     want = balance.sequence_balance_loss(logits.numpy().astype(np.float64), idx.numpy(), score, 1e-3, seq_len)
     got = loss.cpu().numpy().astype(np.float64)
     assert np.allclose(got, want, rtol=2e-6, atol=0)
+    # a second call on a workspace full of NaN bytes: the partials are fully rewritten
+    ws = torch.full((B.moe_balance_loss_workspace_size(cfg, T, seq_len),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
     loss2 = torch.empty_like(loss)
-    B.moe_balance_loss(cfg, T, seq_len, logits.cuda(), idx.cuda(), 1e-3, loss2)
+    B.moe_balance_loss(cfg, T, seq_len, logits.cuda(), idx.cuda(), 1e-3, loss2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(loss, loss2)
 
