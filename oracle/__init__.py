@@ -1,4 +1,4 @@
-"""CPU float64 oracle for the DeepSeekMoE layer forward.
+"""CPU float64 oracle for the DeepSeekMoE layer (forward, backward, balance terms, W8A8).
 
 TEST INFRASTRUCTURE: imported only by the tests, the package entry file's smoke
 check and the benchmark's CPU-baseline leg.  The library never imports it.
