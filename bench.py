@@ -241,6 +241,47 @@ def time_balance_loss(p: Pass, shape, calls: int = 20):
             "us_per_call": us, "bytes_per_call": nbytes, "gbs": nbytes / us / 1e3}
 
 
+def time_backward(p: Pass, shape, calls: int = 3):
+    """The layer backward (moe_backward) of the last timed batch, for a seeded upstream gradient.
+
+    Its GEMM work: the gate/up products again (a and c are recomputed, the
+    forward keeps only h), dH and dX through W2 and W13, and the weight
+    gradients dW2 and dW13, for the routed pairs and the shared expert, plus
+    dX and dW_g of the gate: 3 x (gate/up flops) + 2 x (down flops) + 4 T E D."""
+    import torch
+    from routed_expert_moe_amd import synth
+    B, L = p.B, p.layer
+    T, E, K, D, I, S = shape.T, shape.n_routed, shape.top_k, shape.dim, shape.inter_dim, shape.n_shared
+    dout = synth.make_dout(shape, device="cuda")
+    grads = B.Grads.empty(p.cfg, T, L.x.dtype)
+    ws = torch.empty(B.moe_backward_workspace_size(p.cfg, T), dtype=torch.uint8, device="cuda")
+    p.step()
+
+    def one():
+        B.moe_backward(p.cfg, T, L.x, p.w, p.r, p.idx, p.tw, p.logits, p.y, dout, grads, workspace=ws)
+    one()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(calls):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / calls
+    P = T * K
+    up = 2 * P * 2 * I * D + 2 * T * 2 * S * I * D
+    down = 2 * P * D * I + 2 * T * D * S * I
+    flops = 3 * up + 2 * down + 4 * T * E * D
+    res = {"what": "moe_backward: dx, dW_gate, routed and shared dW13/dW2 for one upstream gradient",
+           "ms_per_call": ms, "tokens_per_s": T / (ms / 1e3), "gemm_flops": flops,
+           "tflops": flops / (ms / 1e3) / 1e12, "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+           "workspace_bytes": ws.numel()}
+    del grads, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(layer, n_tokens: int):
     """The float64 oracle on the first n_tokens tokens of the same workload, on host cores."""
     import numpy as np
@@ -322,6 +363,8 @@ def main():
     }
     res["bias_update"] = time_bias_update(p, shape)
     res["balance_loss"] = time_balance_loss(p, shape)
+    progress("timing the backward")
+    res["backward"] = time_backward(p, shape)
     del p
     torch.cuda.empty_cache()
 

@@ -265,6 +265,52 @@ moe_status moe_balance_loss(const moe_config *cfg, int64_t T, int32_t seq_len, c
 moe_status moe_balance_loss_workspace_size(const moe_config *cfg, int64_t T, int32_t seq_len,
                                            size_t *bytes);
 
+/* ---- the layer backward ------------------------------------------------------ */
+
+/* Gradients of a scalar loss L with upstream gradient dout = dL/d(out), for the
+ * layer the forward entry points compute (notes page: total-output equation,
+ * gate flow steps 1-5, SwiGLU experts).  The chain rule of those steps:
+ *   combine  dw[t,k] = <dout_t, y_pairs[row(t,k)]>,  dy = w[t,k] dout_t
+ *   experts  a = W1_e x_t, c = W3_e x_t (recomputed), h = silu(a) c,
+ *            dh = dy W2_e, da = dh c silu'(a), dc = dh silu(a),
+ *            dW2_e = sum dy h^T, dW1_e = sum da x^T, dW3_e = sum dc x^T,
+ *            dx_t += da W1_e + dc W3_e;  the shared expert likewise with dz = dout
+ *   gate     ds at the chosen experts from dw through route_scale and the
+ *            renormalisation (per norm_topk); dlogits = ds s(1-s) (sigmoid) or
+ *            s (ds - <ds, s>) (softmax); dx += dlogits W_g, dW_g = dlogits^T x
+ *   residual dx += dout when add_residual.
+ * The selection (top-k over s + b, group masking) is piecewise constant: no
+ * gradient flows through it, and the bias gets none.  bf16 activations and bf16
+ * weights only (MOE_ERR_UNSUPPORTED otherwise); dim, inter_dim and n_routed
+ * must be multiples of 8.  GEMMs run on bf16 operands with fp32 accumulation;
+ * dy, h, da/dc and dlogits are rounded to bf16 as GEMM operands.
+ *   x [T, D], w (w_gate, w13, w2, sw13, sw2 as in the forward), r / topk_idx /
+ *   topk_w / logits / y_pairs: exactly what moe_gate, moe_permute and
+ *   moe_expert_ffn produced for this batch; dout [T, D] act dtype.
+ *   grads: caller-owned outputs, fully overwritten (experts that no token chose
+ *   get zero gradients):
+ *     dx [T, D] act dtype;  dw_gate [E, D] fp32;  dw13 [E, 2I, D] fp32;
+ *     dw2 [E, D, I] fp32;  dsw13 [2SI, D] fp32, dsw2 [D, SI] fp32 (n_shared > 0,
+ *     else ignored).
+ *   workspace: device memory of >= moe_backward_workspace_size bytes, 256-byte
+ *   aligned; no initial contents needed.  Operand pointers 16-byte aligned.
+ * Results are the same on every run (no atomics; fixed summation orders). */
+typedef struct moe_grads {
+  void *dx;
+  float *dw_gate;
+  float *dw13;
+  float *dw2;
+  float *dsw13;
+  float *dsw2;
+} moe_grads;
+
+moe_status moe_backward_workspace_size(const moe_config *cfg, int64_t T, size_t *bytes);
+moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                        const moe_routing *r, const int32_t *topk_idx, const float *topk_w,
+                        const float *logits, const void *y_pairs, const void *dout,
+                        const moe_grads *grads, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

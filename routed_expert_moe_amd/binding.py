@@ -60,10 +60,15 @@ class moe_routing(ctypes.Structure):
                                                "act_q", "act_s")]
 
 
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dw_gate", "dw13", "dw2", "dsw13", "dsw2")]
+
+
 EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspace_size",
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update",
-            "moe_quant_act", "moe_balance_loss", "moe_balance_loss_workspace_size")
+            "moe_quant_act", "moe_balance_loss", "moe_balance_loss_workspace_size",
+            "moe_backward", "moe_backward_workspace_size")
 
 _lib = None
 
@@ -97,6 +102,9 @@ def lib():
         "moe_quant_act": [cfgp, I64, P, ctypes.POINTER(moe_routing), P],
         "moe_balance_loss": [cfgp, I64, ctypes.c_int32, P, P, ctypes.c_float, P, ctypes.c_size_t, P, P],
         "moe_balance_loss_workspace_size": [cfgp, I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+        "moe_backward_workspace_size": [cfgp, I64, ctypes.POINTER(SZ)],
+        "moe_backward": [cfgp, I64, P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing), P, P, P,
+                         P, P, ctypes.POINTER(moe_grads), P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -270,6 +278,45 @@ def moe_balance_loss(cfg: moe_config, T: int, seq_len: int, logits, topk_idx, al
     _check(lib().moe_balance_loss(ctypes.byref(cfg), T, int(seq_len), _ptr(logits), _ptr(topk_idx),
                                   float(alpha), _ptr(workspace), _nbytes(workspace), _ptr(loss),
                                   _stream(stream)))
+
+
+def moe_backward_workspace_size(cfg: moe_config, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_backward_workspace_size(ctypes.byref(cfg), T, ctypes.byref(n)))
+    return n.value
+
+
+@dataclass
+class Grads:
+    """Gradient buffers of moe_backward (device tensors)."""
+    dx: torch.Tensor         # [T, D] act dtype
+    dw_gate: torch.Tensor    # [E, D] fp32
+    dw13: torch.Tensor       # [E, 2I, D] fp32
+    dw2: torch.Tensor        # [E, D, I] fp32
+    dsw13: Optional[torch.Tensor] = None   # [2SI, D] fp32
+    dsw2: Optional[torch.Tensor] = None    # [D, SI] fp32
+
+    @staticmethod
+    def empty(cfg: moe_config, T: int, act_dtype, device="cuda") -> "Grads":
+        D, E, I, SI = cfg.dim, cfg.n_routed, cfg.inter_dim, cfg.n_shared * cfg.inter_dim
+        f = dict(dtype=torch.float32, device=device)
+        return Grads(torch.empty(T, D, dtype=act_dtype, device=device), torch.empty(E, D, **f),
+                     torch.empty(E, 2 * I, D, **f), torch.empty(E, D, I, **f),
+                     torch.empty(2 * SI, D, **f) if SI else None, torch.empty(D, SI, **f) if SI else None)
+
+    def struct(self) -> moe_grads:
+        return moe_grads(*(_ptr(t) for t in (self.dx, self.dw_gate, self.dw13, self.dw2, self.dsw13, self.dsw2)))
+
+
+def moe_backward(cfg: moe_config, T: int, x, weights: moe_weights, routing: Routing, topk_idx, topk_w,
+                 logits, y_pairs, dout, grads: Grads, workspace=None, stream=None) -> None:
+    """workspace: a device buffer of >= moe_backward_workspace_size bytes (allocated here if None)."""
+    if workspace is None:
+        workspace = _device_bytes(moe_backward_workspace_size(cfg, T), x)
+    g = grads.struct()
+    _check(lib().moe_backward(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(weights), ctypes.byref(routing.struct),
+                              _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(y_pairs), _ptr(dout),
+                              ctypes.byref(g), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def moe_bias_update(cfg: moe_config, T: int, routing: Routing, gamma: float, bias, stream=None) -> None:

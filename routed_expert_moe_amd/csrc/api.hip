@@ -376,6 +376,68 @@ moe_status check_weights(const moe_config &c, const moe_weights *w, bool need_sh
   return MOE_OK;
 }
 
+
+// ---- backward workspace ------------------------------------------------------
+struct BwdLayout {
+  RoutingLayout rl;
+  int64_t tcap;   // 128-row tile capacity
+  size_t off_trow, off_texp, off_tend, off_nt, off_ab, off_dy, off_dh, off_h, off_dab, off_dxp, off_dw,
+      off_dl, off_dxg, off_abs, off_dhs, off_hsb, off_dabs, off_dxs, total;
+};
+
+BwdLayout bwd_layout(const moe_config &c, int64_t T) {
+  BwdLayout L{};
+  L.rl = routing_layout(c, T);
+  const size_t MR = static_cast<size_t>(L.rl.max_rows), D = c.dim, I = c.inter_dim, E = c.n_routed,
+               K = c.top_k, SI = static_cast<size_t>(c.n_shared) * c.inter_dim, Tz = static_cast<size_t>(T);
+  L.tcap = L.rl.max_rows / 128 + 1 + c.n_routed;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = round_up(o + bytes, kAlign);
+    return at;
+  };
+  L.off_trow = take(4 * static_cast<size_t>(L.tcap));
+  L.off_texp = take(4 * static_cast<size_t>(L.tcap));
+  L.off_tend = take(4 * static_cast<size_t>(L.tcap));
+  L.off_nt = take(4);
+  L.off_ab = take(4 * MR * 2 * I);
+  L.off_dy = take(2 * MR * D);
+  L.off_dh = take(4 * MR * I);
+  L.off_h = take(2 * MR * I);
+  L.off_dab = take(2 * MR * 2 * I);
+  L.off_dxp = take(4 * MR * D);
+  L.off_dw = take(4 * Tz * K);
+  L.off_dl = take(2 * Tz * E);
+  L.off_dxg = take(4 * Tz * D);
+  L.off_abs = take(4 * Tz * 2 * SI);
+  L.off_dhs = take(4 * Tz * SI);
+  L.off_hsb = take(2 * Tz * SI);
+  L.off_dabs = take(2 * Tz * 2 * SI);
+  L.off_dxs = take(4 * Tz * D);
+  L.total = o;
+  return L;
+}
+
+moe_status check_bwd_cfg(const moe_config &c) {
+  if (c.act_dtype != MOE_BF16 || c.weight_dtype != MOE_BF16 || c.act_quant)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass supports bf16 activations and bf16 weights only");
+  if (c.dim % 8 || c.inter_dim % 8 || c.n_routed % 8)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs dim, inter_dim and n_routed multiples of 8");
+  return MOE_OK;
+}
+
+// C = A B^T with fp32 output (EPI_STORE) on the forward GEMM the plan picks
+hipError_t store_gemm_f32(const Plan &p, Segment *segs, int nseg, hipStream_t st) {
+  switch (p.path) {
+    case PATH_MFMA:
+      if (gemm_mfma2_supported(segs, nseg)) return launch_gemm_mfma2(segs, nseg, EPI_STORE, true, st);
+      return launch_gemm_mfma(segs, nseg, p.tile_m, EPI_STORE, true, st);
+    case PATH_SKINNY: return launch_gemm_skinny(segs, nseg, EPI_STORE, false, true, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -639,6 +701,263 @@ moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const mo
   MOE_TRY(do_ffn(c, T, x, r, *w, h, y, shared ? hs : nullptr, shared ? z : nullptr, st));
   e = launch_combine(c, T, x, shared ? z : nullptr, y, r, wt, out, st);
   if (e != hipSuccess) return device_fail(e, "combine launch");
+  return ok();
+}
+
+
+moe_status moe_backward_workspace_size(const moe_config *cfg, int64_t T, size_t *bytes) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_bwd_cfg(*cfg));
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = bwd_layout(*cfg, T).total;
+  return ok();
+}
+
+moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                        const moe_routing *r, const int32_t *topk_idx, const float *topk_w,
+                        const float *logits, const void *y_pairs, const void *dout, const moe_grads *g,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_bwd_cfg(*cfg));
+  const moe_config &c = *cfg;
+  const bool shared = c.n_shared > 0;
+  MOE_TRY(check_weights(c, w, shared));
+  MOE_NEED(w->w_gate, "w_gate");
+  MOE_TRY(check_routing(c, T, r));
+  if (g == nullptr) return fail(MOE_ERR_INVALID_ARG, "grads is NULL");
+  MOE_NEED(x, "x");
+  MOE_NEED(topk_idx, "topk_idx");
+  MOE_NEED(topk_w, "topk_w");
+  MOE_NEED(logits, "logits");
+  MOE_NEED(y_pairs, "y_pairs");
+  MOE_NEED(dout, "dout");
+  MOE_NEED(g->dx, "grads->dx");
+  MOE_NEED(g->dw_gate, "grads->dw_gate");
+  MOE_NEED(g->dw13, "grads->dw13");
+  MOE_NEED(g->dw2, "grads->dw2");
+  if (shared) {
+    MOE_NEED(g->dsw13, "grads->dsw13");
+    MOE_NEED(g->dsw2, "grads->dsw2");
+  }
+  const void *vec[] = {x, w->w_gate, w->w13, w->w2, y_pairs, dout, g->dx, g->dw_gate, g->dw13, g->dw2};
+  for (const void *q : vec)
+    if (!aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "x, weights, y_pairs, dout and the gradients must be 16-byte aligned");
+  if (shared && (!aligned16(w->sw13) || !aligned16(w->sw2) || !aligned16(g->dsw13) || !aligned16(g->dsw2)))
+    return fail(MOE_ERR_INVALID_ARG, "shared weights and gradients must be 16-byte aligned");
+  if (T == 0) return ok();
+  const BwdLayout L = bwd_layout(c, T);
+  if (workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(MOE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "backward workspace too small: %zu < %zu", workspace_bytes, L.total);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  const Plan p = plan_for(c, T);
+  const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim,
+                E = c.n_routed, K = c.top_k;
+  int32_t *trow = static_cast<int32_t *>(at(L.off_trow)), *texp = static_cast<int32_t *>(at(L.off_texp)),
+          *tend = static_cast<int32_t *>(at(L.off_tend)), *nt = static_cast<int32_t *>(at(L.off_nt));
+  float *ab = static_cast<float *>(at(L.off_ab)), *dh = static_cast<float *>(at(L.off_dh)),
+        *dxp = static_cast<float *>(at(L.off_dxp)), *dw = static_cast<float *>(at(L.off_dw)),
+        *dxg = static_cast<float *>(at(L.off_dxg)), *abs_ = static_cast<float *>(at(L.off_abs)),
+        *dhs = static_cast<float *>(at(L.off_dhs)), *dxs = static_cast<float *>(at(L.off_dxs));
+  void *dy = at(L.off_dy), *hb = at(L.off_h), *dab = at(L.off_dab), *dl = at(L.off_dl), *hsb = at(L.off_hsb),
+       *dabs = at(L.off_dabs);
+  auto bf = [](const void *q) { return static_cast<const uint16_t *>(q); };
+  hipError_t e = hipSuccess;
+#define MOE_BWD(call, what) \
+  do {                      \
+    e = (call);             \
+    if (e != hipSuccess) return device_fail(e, what); \
+  } while (0)
+
+  // 1. a, c of every used row again (the forward kept only h): [rows, 2I] fp32
+  Segment up[2] = {};
+  up[0].a = x;
+  up[0].lda = D;
+  up[0].gather = r->sorted_pair;
+  up[0].topk = c.top_k;
+  up[0].b = w->w13;
+  up[0].b_stride = 2 * I * D;
+  up[0].n = static_cast<int32_t>(2 * I);
+  up[0].k = static_cast<int32_t>(D);
+  up[0].c = ab;
+  up[0].ldc = 2 * I;
+  up[0].tile_row = r->tile_row;
+  up[0].tile_expert = r->tile_expert;
+  up[0].expert_off = r->expert_off;
+  up[0].n_tiles_dev = r->n_tiles;
+  up[0].n_tiles_host = r->max_tiles;
+  int nseg = 1;
+  if (shared) {
+    nseg = 2;
+    up[1].a = x;
+    up[1].lda = D;
+    up[1].a_rows = static_cast<int32_t>(T);
+    up[1].b = w->sw13;
+    up[1].n = static_cast<int32_t>(2 * SI);
+    up[1].k = static_cast<int32_t>(D);
+    up[1].c = abs_;
+    up[1].ldc = 2 * SI;
+    up[1].n_tiles_host = static_cast<int32_t>((T + p.tile_m - 1) / p.tile_m);
+  }
+  MOE_BWD(store_gemm_f32(p, up, nseg, st), "backward gate/up recompute launch");
+  MOE_BWD(launch_bwd_tiles(r->expert_off, c.n_routed, trow, texp, tend, nt, st), "backward tile list launch");
+
+  // 2. combine: dw, dy
+  MOE_BWD(launch_combine_bwd(dout, y_pairs, *r, topk_w, c.top_k, c.dim, dy, dw, st), "combine backward launch");
+
+  // 3. routed experts: dh = dy W2_e, SwiGLU backward, dx_pairs = dab W13_e, dW2, dW13
+  BwdGemm rg{};
+  rg.mode = BWD_ROWS;
+  rg.tile_row = trow;
+  rg.tile_expert = texp;
+  rg.tile_end = tend;
+  rg.n_tiles_dev = nt;
+  rg.n_tiles_host = static_cast<int32_t>(L.tcap);
+  BwdGemm q = rg;
+  q.a = bf(dy);
+  q.lda = D;
+  q.b = bf(w->w2);
+  q.ldb = I;
+  q.b_estride = D * I;
+  q.c = dh;
+  q.ldc = I;
+  q.n = static_cast<int32_t>(I);
+  q.k = static_cast<int32_t>(D);
+  MOE_BWD(launch_gemm_bwd(q, 1, st), "backward dh launch");
+  MOE_BWD(launch_swiglu_bwd(ab, dh, r->n_tiles, r->tile_m, r->max_rows, static_cast<int>(I), hb, dab, st),
+          "backward SwiGLU launch");
+  q = rg;
+  q.a = bf(dab);
+  q.lda = 2 * I;
+  q.b = bf(w->w13);
+  q.ldb = D;
+  q.b_estride = 2 * I * D;
+  q.c = dxp;
+  q.ldc = D;
+  q.n = static_cast<int32_t>(D);
+  q.k = static_cast<int32_t>(2 * I);
+  MOE_BWD(launch_gemm_bwd(q, 1, st), "backward dx launch");
+  BwdGemm wg{};
+  wg.mode = BWD_WGRAD;
+  wg.expert_off = r->expert_off;
+  q = wg;
+  q.a = bf(dy);
+  q.lda = D;
+  q.b = bf(hb);
+  q.ldb = I;
+  q.c = g->dw2;
+  q.ldc = I;
+  q.c_estride = D * I;
+  q.m = static_cast<int32_t>(D);
+  q.n = static_cast<int32_t>(I);
+  MOE_BWD(launch_gemm_bwd(q, c.n_routed, st), "backward dW2 launch");
+  q = wg;
+  q.a = bf(dab);
+  q.lda = 2 * I;
+  q.b = bf(x);
+  q.ldb = D;
+  q.b_gather = r->sorted_pair;
+  q.topk = c.top_k;
+  q.c = g->dw13;
+  q.ldc = D;
+  q.c_estride = 2 * I * D;
+  q.m = static_cast<int32_t>(2 * I);
+  q.n = static_cast<int32_t>(D);
+  MOE_BWD(launch_gemm_bwd(q, c.n_routed, st), "backward dW13 launch");
+
+  // 4. shared expert: dz = dout
+  if (shared) {
+    BwdGemm dg{};
+    dg.mode = BWD_ROWS;
+    dg.dense_rows = static_cast<int32_t>(T);
+    q = dg;
+    q.a = bf(dout);
+    q.lda = D;
+    q.b = bf(w->sw2);
+    q.ldb = SI;
+    q.c = dhs;
+    q.ldc = SI;
+    q.n = static_cast<int32_t>(SI);
+    q.k = static_cast<int32_t>(D);
+    MOE_BWD(launch_gemm_bwd(q, 1, st), "backward shared dh launch");
+    MOE_BWD(launch_swiglu_bwd(abs_, dhs, nullptr, 0, T, static_cast<int>(SI), hsb, dabs, st),
+            "backward shared SwiGLU launch");
+    q = dg;
+    q.a = bf(dabs);
+    q.lda = 2 * SI;
+    q.b = bf(w->sw13);
+    q.ldb = D;
+    q.c = dxs;
+    q.ldc = D;
+    q.n = static_cast<int32_t>(D);
+    q.k = static_cast<int32_t>(2 * SI);
+    MOE_BWD(launch_gemm_bwd(q, 1, st), "backward shared dx launch");
+    BwdGemm dw1{};
+    dw1.mode = BWD_WGRAD;
+    dw1.dense_rows = static_cast<int32_t>(T);
+    q = dw1;
+    q.a = bf(dout);
+    q.lda = D;
+    q.b = bf(hsb);
+    q.ldb = SI;
+    q.c = g->dsw2;
+    q.ldc = SI;
+    q.m = static_cast<int32_t>(D);
+    q.n = static_cast<int32_t>(SI);
+    MOE_BWD(launch_gemm_bwd(q, 1, st), "backward shared dW2 launch");
+    q = dw1;
+    q.a = bf(dabs);
+    q.lda = 2 * SI;
+    q.b = bf(x);
+    q.ldb = D;
+    q.c = g->dsw13;
+    q.ldc = D;
+    q.m = static_cast<int32_t>(2 * SI);
+    q.n = static_cast<int32_t>(D);
+    MOE_BWD(launch_gemm_bwd(q, 1, st), "backward shared dW13 launch");
+  }
+
+  // 5. gate: dlogits, dx_gate = dl W_g, dW_g = dl^T x
+  MOE_BWD(launch_gate_bwd(c, T, logits, topk_idx, r->pair_row, dw, dl, st), "gate backward launch");
+  {
+    BwdGemm dg{};
+    dg.mode = BWD_ROWS;
+    dg.dense_rows = static_cast<int32_t>(T);
+    dg.a = bf(dl);
+    dg.lda = E;
+    dg.b = bf(w->w_gate);
+    dg.ldb = D;
+    dg.c = dxg;
+    dg.ldc = D;
+    dg.n = static_cast<int32_t>(D);
+    dg.k = static_cast<int32_t>(E);
+    MOE_BWD(launch_gemm_bwd(dg, 1, st), "gate dx launch");
+    BwdGemm gw{};
+    gw.mode = BWD_WGRAD;
+    gw.dense_rows = static_cast<int32_t>(T);
+    gw.a = bf(dl);
+    gw.lda = E;
+    gw.b = bf(x);
+    gw.ldb = D;
+    gw.c = g->dw_gate;
+    gw.ldc = D;
+    gw.m = static_cast<int32_t>(E);
+    gw.n = static_cast<int32_t>(D);
+    MOE_BWD(launch_gemm_bwd(gw, 1, st), "gate dW launch");
+  }
+
+  // 6. the tokens' gradient
+  MOE_BWD(launch_dx_final(T, static_cast<int>(K), static_cast<int>(D), c.add_residual, dout,
+                          shared ? dxs : nullptr, dxp, dxg, r->pair_row, g->dx, st),
+          "backward dx launch");
+#undef MOE_BWD
   return ok();
 }
 

@@ -1,0 +1,218 @@
+// Grouped GEMMs of the layer's backward pass on bf16 MFMA, fp32 results.
+//
+// Two forms, both over bf16 operands stored row-major:
+//   ROWS   C[r, n] = sum_k A[r, k] B_e[k, n]     (r: rows of a 128-row tile of
+//          expert e's rows, or of a dense row range).  dH = dY W2_e,
+//          dX = dAB W13_e, and the shared expert's and the gate's counterparts.
+//   WGRAD  C_e[m, n] = sum_r A[r, m] B[g(r), n] over the rows r of expert e
+//          (or all rows of a dense segment).  dW2_e = dY_e^T H_e,
+//          dW13_e = dAB_e^T X_e (g gathers the token of each row), and the
+//          shared expert's and the gate's weight gradients.
+//
+// Workgroup tile 128 x 128, K step 32, four wavefronts in a 2 x 2 arrangement,
+// each owning 64 x 64 of C as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Both
+// operands are staged in LDS as [row][k] (k contiguous, rows padded to 80
+// bytes so the 16-byte fragment reads of 8 consecutive rows hit distinct
+// banks).  An operand whose k index is its contiguous one (A in ROWS) is copied
+// 16 bytes at a time; one whose k index is its row index (B in ROWS, both in
+// WGRAD) is transposed on the way: each thread reads the same 16-byte column
+// piece of rows k and k+1 and writes eight (k, k+1) bf16 pairs as dwords.  The
+// next step's global loads are issued before the current step's MFMAs.
+//
+// Rows past a tile's end are read (clamped to a valid row) but never stored; a
+// WGRAD segment with no rows stores zeros.  Requires every k-contiguous extent
+// and every column count to be a multiple of 8.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int kThreads = 256;
+constexpr int kLdsRow = 40;                  // bf16 per LDS row (32 + 8 pad = 80 bytes)
+constexpr int kTileElems = 128 * kLdsRow;
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// a [32 k] x [128 cols] slab of a matrix whose rows are k: thread t takes the
+// k pair 2 * (t % 16) and the 8 columns 8 * (t / 16)
+struct SlabT {
+  u32x4_t v0, v1;
+};
+// a [128 rows] x [32 k] slab of a matrix whose rows are the tile rows: thread t
+// takes chunks t and t + 256 (row c / 4, k 8 * (c % 4))
+struct SlabK {
+  u32x4_t v[2];
+};
+
+__device__ __forceinline__ void store_t(uint16_t *s, const SlabT &x, int tid) {
+  const int kp = tid & 15, cc = tid >> 4;
+  uint32_t *d = reinterpret_cast<uint32_t *>(s);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo = (x.v0[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const uint32_t hi = (x.v1[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    d[((cc * 8 + i) * kLdsRow + 2 * kp) >> 1] = lo | (hi << 16);
+  }
+}
+__device__ __forceinline__ void store_k(uint16_t *s, const SlabK &x, int tid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + kThreads * j;
+    *reinterpret_cast<u32x4_t *>(s + (c >> 2) * kLdsRow + 8 * (c & 3)) = x.v[j];
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void gemm_bwd_kernel(BwdGemm g) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[kTileElems];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint16_t *A = g.a;
+  const uint16_t *B = g.b;
+
+  int m0, n0, row_end = 0, k_begin, k_end, e = 0;
+  if (MODE == BWD_ROWS) {
+    const int nbn = (g.n + BN - 1) / BN;
+    const int ti = blockIdx.x / nbn;
+    n0 = (blockIdx.x - ti * nbn) * BN;
+    const int ntiles = g.n_tiles_dev ? *g.n_tiles_dev : (g.dense_rows + BM - 1) / BM;
+    if (ti >= ntiles) return;
+    if (g.n_tiles_dev) {
+      m0 = g.tile_row[ti];
+      e = g.tile_expert[ti];
+      row_end = g.tile_end[ti];
+    } else {
+      m0 = ti * BM;
+      row_end = g.dense_rows;
+    }
+    B += static_cast<int64_t>(e) * g.b_estride;
+    k_begin = 0;
+    k_end = g.k;
+  } else {
+    const int nbm = (g.m + BM - 1) / BM, nbn = (g.n + BN - 1) / BN;
+    e = blockIdx.x / (nbm * nbn);
+    const int rem = blockIdx.x - e * nbm * nbn;
+    m0 = (rem / nbn) * BM;
+    n0 = (rem % nbn) * BN;
+    k_begin = g.expert_off ? g.expert_off[e] : 0;
+    k_end = g.expert_off ? g.expert_off[e + 1] : g.dense_rows;
+  }
+  m0 = uniform(m0);
+  n0 = uniform(n0);
+  k_begin = uniform(k_begin);
+  k_end = uniform(k_end);
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+
+  // ---- global -> register loads of one K step
+  // ROWS A: rows m0 + r (clamped below row_end), k contiguous
+  auto load_ak = [&](int k0, SlabK &x) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = tid + kThreads * j;
+      int r = m0 + (c >> 2);
+      if (r >= row_end) r = row_end - 1;
+      const int k = k0 + 8 * (c & 3);
+      x.v[j] = k < k_end ? *reinterpret_cast<const u32x4_t *>(A + static_cast<int64_t>(r) * g.lda + k)
+                         : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  // a matrix whose rows are k: columns [c0, c0 + 128) of rows k0 .. k0 + 31,
+  // `ncols` valid columns, row index mapped through the gather for B in WGRAD
+  auto load_t = [&](const uint16_t *M, int64_t ld, int ncols, int c0, int k0, bool gather, SlabT &x) {
+    const int kp = tid & 15, cc = tid >> 4;
+    const int col = c0 + cc * 8;
+    const int k = k0 + 2 * kp;
+    auto row_of = [&](int kk) -> int64_t {
+      if (!gather) return kk;
+      const int p = g.b_gather[kk];
+      return p >= 0 ? p / g.topk : 0;
+    };
+    const bool cin = col < ncols;
+    x.v0 = (cin && k < k_end) ? *reinterpret_cast<const u32x4_t *>(M + row_of(k) * ld + col) : u32x4_t{0, 0, 0, 0};
+    x.v1 = (cin && k + 1 < k_end) ? *reinterpret_cast<const u32x4_t *>(M + row_of(k + 1) * ld + col)
+                                  : u32x4_t{0, 0, 0, 0};
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  SlabK ak;
+  SlabT at, bt;
+  auto load = [&](int kt) {
+    const int k0 = k_begin + kt * BK;
+    if (MODE == BWD_ROWS) {
+      load_ak(k0, ak);
+      load_t(B, g.ldb, g.n, n0, k0, false, bt);
+    } else {
+      load_t(A, g.lda, g.m, m0, k0, false, at);
+      load_t(B, g.ldb, g.n, n0, k0, g.b_gather != nullptr, bt);
+    }
+  };
+
+  if (nk > 0) load(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();   // the previous step's fragment reads are done
+    if (MODE == BWD_ROWS) store_k(s_a, ak, tid);
+    else store_t(s_a, at, tid);
+    store_t(s_b, bt, tid);
+    __syncthreads();
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      bf16x8_t af[2], bf[2];
+      const int kk = s * 16 + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8_t *>(s_a + (wm * 64 + i * 32 + (lane & 31)) * kLdsRow + kk);
+        bf[i] = *reinterpret_cast<const bf16x8_t *>(s_b + (wn * 64 + i * 32 + (lane & 31)) * kLdsRow + kk);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- store: acc[i][j][r] is C[m0 + wm*64 + i*32 + 8*(r/4) + 4*(lane/32) + r%4][n0 + wn*64 + j*32 + lane%32]
+  float *C = g.c + (MODE == BWD_WGRAD ? static_cast<int64_t>(e) * g.c_estride : 0);
+  const int mlim = MODE == BWD_ROWS ? row_end : g.m;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (n >= g.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < mlim) C[static_cast<int64_t>(m) * g.ldc + n] = acc[i][j][r];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bwd(const BwdGemm &g, int groups, hipStream_t st) {
+  if (g.mode == BWD_ROWS) {
+    const int nbn = (g.n + BN - 1) / BN;
+    const int64_t tiles = g.n_tiles_dev ? g.n_tiles_host : (g.dense_rows + BM - 1) / BM;
+    const int64_t blocks = tiles * nbn;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_bwd_kernel<BWD_ROWS>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, g);
+  } else {
+    const int64_t blocks = static_cast<int64_t>(groups) * ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_bwd_kernel<BWD_WGRAD>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

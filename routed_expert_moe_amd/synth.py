@@ -35,7 +35,7 @@ FP8_MAX = 448.0
 FP8_BLOCK = 128
 
 _TENSOR_IDS = {"x": 1, "w_gate": 2, "bias": 3, "w13": 4, "w2": 5,
-               "sw13": 6, "sw2": 7, "zipf": 8}
+               "sw13": 6, "sw2": 7, "zipf": 8, "dout": 9}
 
 _TORCH_ACT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -102,6 +102,13 @@ def zipf_row_scale(shape: LayerShape, device) -> torch.Tensor:
 def make_x(shape: LayerShape, device, T: Optional[int] = None, seed_offset: int = 0) -> torch.Tensor:
     T = shape.T if T is None else T
     g = _gen(device, shape.seed + seed_offset, "x")
+    return _normal((T, shape.dim), 1.0, device, g).to(_TORCH_ACT[shape.act])
+
+
+def make_dout(shape: LayerShape, device="cpu", T: Optional[int] = None) -> torch.Tensor:
+    """Upstream gradient dL/d(out) for the backward pass: N(0, 1), [T, dim] in the act dtype."""
+    T = shape.T if T is None else T
+    g = _gen(device, shape.seed, "dout")
     return _normal((T, shape.dim), 1.0, device, g).to(_TORCH_ACT[shape.act])
 
 

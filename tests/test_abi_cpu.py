@@ -178,3 +178,35 @@ def test_routing_layout_is_aligned_and_disjoint():
         assert spans[-1][0] < base + n
         assert r.max_rows % r.tile_m == 0 and r.max_rows >= P + shape.n_routed * (r.tile_m - 1)
         assert r.max_tiles * r.tile_m == r.max_rows
+
+
+def test_backward_validates_before_launch():
+    L = B.lib()
+    fake = 1 << 20
+    c = B.config_of(configs.V2_LITE_BF16)
+    T = 64
+    need = B.moe_backward_workspace_size(c, T)
+    r = B.moe_routing_init(c, T, fake, B.moe_routing_size(c, T))
+    w = B.moe_weights(w_gate=fake, w13=fake, w2=fake, sw13=fake, sw2=fake)
+    g = B.moe_grads(dx=fake, dw_gate=fake, dw13=fake, dw2=fake, dsw13=fake, dsw2=fake)
+    ws = 1 << 32
+
+    def call(cfg=c, T=T, wts=w, grads=g, dout=fake, wsp=ws, nb=need):
+        return L.moe_backward(ctypes.byref(cfg), T, fake, ctypes.byref(wts), ctypes.byref(r), fake, fake, fake,
+                              fake, dout, ctypes.byref(grads), wsp, nb, None)
+    assert call(dout=None) == B.MOE_ERR_INVALID_ARG
+    assert call(grads=B.moe_grads(dx=fake, dw_gate=fake, dw13=fake, dw2=None, dsw13=fake, dsw2=fake)) == B.MOE_ERR_INVALID_ARG
+    assert call(grads=B.moe_grads(dx=fake, dw_gate=fake, dw13=fake, dw2=fake)) == B.MOE_ERR_INVALID_ARG  # shared grads
+    assert call(wsp=None) == B.MOE_ERR_INVALID_ARG
+    assert call(wsp=ws + 64) == B.MOE_ERR_INVALID_ARG
+    assert call(nb=need - 1) == B.MOE_ERR_WORKSPACE
+    assert call(dout=fake + 8) == B.MOE_ERR_INVALID_ARG                    # 16-byte alignment
+    for bad in (B.config_of(configs.TINY_F32), B.config_of(configs.V3_DECODE_FP8)):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_backward_workspace_size(bad, 8)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+    r0 = B.moe_routing_init(c, 0, fake, B.moe_routing_size(c, 0))
+    assert L.moe_backward(ctypes.byref(c), 0, fake, ctypes.byref(w), ctypes.byref(r0), fake, fake, fake, fake,
+                          fake, ctypes.byref(g), None, 0, None) == B.MOE_OK
+    # the workspace grows with T and holds the 128-row tile lists, fp32 a/c, dh, dx per routed row
+    assert B.moe_backward_workspace_size(c, 2 * T) > need
