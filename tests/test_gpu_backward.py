@@ -127,3 +127,48 @@ def test_backward_rejects_unsupported_and_small_workspace():
     with pytest.raises(B.MoeError) as ei:
         B.moe_backward_workspace_size(f32, s.T)
     assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_backward_v3_prefill_sampled():
+    """The V3 prefill layer at its full size (T=8192, the batch bench.py times):
+    dx on a seeded sample of tokens and dW13 / dW2 of one expert, against the
+    oracle computed for just those outputs (each depends only on the sampled
+    token's own pairs, or on the rows the expert received)."""
+    import oracle
+    from routed_expert_moe_amd import configs
+    s = configs.V3_PREFILL_BF16
+    say("[moe_backward] v3 prefill T=8192, sampled")
+    layer = synth.make_layer(s, device="cuda")
+    dout = synth.make_dout(s, device="cuda")
+    fwd = _forward(layer)
+    g = _backward(layer, *fwd, dout)
+    idx = fwd[3].cpu().numpy().astype(np.int64)
+    spec = spec_of(s)
+    x64 = to_f64(layer.x)
+    wg64 = to_f64(layer.w_gate)
+    d64 = to_f64(dout)
+    get = expert_fn(layer)
+    sh = shared_pair(layer)
+
+    # dx of sampled tokens: the oracle's backward restricted to those tokens is
+    # exact, since dx_t only involves token t's gate row, experts and dout_t
+    rng = np.random.default_rng(2024)
+    toks = np.sort(rng.choice(s.T, 12, replace=False))
+    want = obw.moe_layer_backward(x64[toks], wg64, bias_f64(layer), get, sh, spec, d64[toks],
+                                  force_idx=idx[toks]).dx
+    err = rel_err(to_f64(g.dx)[toks], want)
+    say(f"  dx (12 tokens) {err:.3g}")
+    assert err <= TOL
+
+    # one expert's weight gradients from every row it received
+    counts = np.bincount(idx.ravel(), minlength=s.n_routed)
+    e = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    rows, slot = np.nonzero(idx == e)
+    gt = oracle.gate(x64, wg64, bias_f64(layer), spec, force_idx=idx)
+    w13, w2 = get(e)
+    dy = gt.w[rows, slot][:, None] * d64[rows]
+    _, dw13, dw2 = obw.swiglu_ffn_backward(x64[rows], w13, w2, dy)
+    e13 = rel_err(g.dw13[e].cpu().numpy(), dw13)
+    e2 = rel_err(g.dw2[e].cpu().numpy(), dw2)
+    say(f"  expert {e} ({rows.size} rows): dw13 {e13:.3g} dw2 {e2:.3g}")
+    assert e13 <= TOL and e2 <= TOL
