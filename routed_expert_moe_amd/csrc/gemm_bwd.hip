@@ -10,14 +10,18 @@
 //          shared expert's and the gate's weight gradients.
 //
 // Workgroup tile 128 x 128, K step 32, four wavefronts in a 2 x 2 arrangement,
-// each owning 64 x 64 of C as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Both
-// operands are staged in LDS as [row][k] (k contiguous, rows padded to 80
-// bytes so the 16-byte fragment reads of 8 consecutive rows hit distinct
-// banks).  An operand whose k index is its contiguous one (A in ROWS) is copied
-// 16 bytes at a time; one whose k index is its row index (B in ROWS, both in
-// WGRAD) is transposed on the way: each thread reads the same 16-byte column
-// piece of rows k and k+1 and writes eight (k, k+1) bf16 pairs as dwords.  The
-// next step's global loads are issued before the current step's MFMAs.
+// each owning 64 x 64 of C as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+// Operands are copied into LDS in their memory layout, 16 bytes per thread
+// and load:
+//  * k-contiguous (A in ROWS) as [row][k], rows padded to 80 bytes, so the
+//    16-byte fragment reads of 8 consecutive rows hit distinct banks;
+//  * k-strided (B in ROWS, both in WGRAD) as [k][col], rows padded to 288
+//    bytes; an MFMA operand (8 consecutive k of one column per lane) is then
+//    read with two ds_read_b64_tr_b16: within each 16-lane group, lane q
+//    addresses 4 columns of row kb + q/4 and lane l receives column l of rows
+//    kb .. kb+3 (the padding puts the four rows' 32-byte pieces on distinct
+//    banks).
+// The next step's global loads are issued before the current step's MFMAs.
 //
 // Rows past a tile's end are read (clamped to a valid row) but never stored; a
 // WGRAD segment with no rows stores zeros.  Requires every k-contiguous extent
@@ -29,15 +33,20 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int kThreads = 256;
-constexpr int kLdsRow = 40;                  // bf16 per LDS row (32 + 8 pad = 80 bytes)
+constexpr int kLdsRow = 40;                  // [row][k] tile: bf16 per row (32 + 8 pad = 80 bytes)
 constexpr int kTileElems = 128 * kLdsRow;
+constexpr int kTRow = 144;                   // [k][col] tile: bf16 per row (128 + 16 pad = 288 bytes)
+constexpr int kTTileElems = BK * kTRow;
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// a [32 k] x [128 cols] slab of a matrix whose rows are k: thread t takes the
-// k pair 2 * (t % 16) and the 8 columns 8 * (t / 16)
+// a [32 k] x [128 cols] slab of a matrix whose rows are k: thread t takes
+// chunks t and t + 256 (row c / 16, columns 8 * (c % 16))
 struct SlabT {
-  u32x4_t v0, v1;
+  u32x4_t v[2];
 };
 // a [128 rows] x [32 k] slab of a matrix whose rows are the tile rows: thread t
 // takes chunks t and t + 256 (row c / 4, k 8 * (c % 4))
@@ -46,14 +55,25 @@ struct SlabK {
 };
 
 __device__ __forceinline__ void store_t(uint16_t *s, const SlabT &x, int tid) {
-  const int kp = tid & 15, cc = tid >> 4;
-  uint32_t *d = reinterpret_cast<uint32_t *>(s);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t lo = (x.v0[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    const uint32_t hi = (x.v1[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    d[((cc * 8 + i) * kLdsRow + 2 * kp) >> 1] = lo | (hi << 16);
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + kThreads * j;
+    *reinterpret_cast<u32x4_t *>(s + (c >> 4) * kTRow + 8 * (c & 15)) = x.v[j];
   }
+}
+// MFMA operand of column block [cb, cb + 32) and K slice [ks, ks + 16) from a
+// [k][col] tile: lane l gets column cb + l % 32, k = ks + 8 * (l / 32) + 0..7
+__device__ __forceinline__ bf16x8_t frag_t(const uint16_t *s, int cb, int ks, int lane) {
+  const int g = lane >> 4, q = lane & 15;
+  const int col = cb + 16 * (g & 1) + 4 * (q & 3);
+  const int kb = ks + 8 * (g >> 1) + (q >> 2);
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(s + kb * kTRow + col));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(s + (kb + 4) * kTRow + col));
+  const u32x4_t v = {static_cast<uint32_t>(static_cast<uint16_t>(lo[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[1])) << 16),
+                     static_cast<uint32_t>(static_cast<uint16_t>(lo[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[3])) << 16),
+                     static_cast<uint32_t>(static_cast<uint16_t>(hi[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[1])) << 16),
+                     static_cast<uint32_t>(static_cast<uint16_t>(hi[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[3])) << 16)};
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 __device__ __forceinline__ void store_k(uint16_t *s, const SlabK &x, int tid) {
 #pragma unroll
@@ -65,8 +85,8 @@ __device__ __forceinline__ void store_k(uint16_t *s, const SlabK &x, int tid) {
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void gemm_bwd_kernel(BwdGemm g) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[MODE == BWD_ROWS ? kTileElems : kTTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[kTTileElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const uint16_t *A = g.a;
@@ -121,18 +141,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bwd_kernel(BwdGemm g) {
   // a matrix whose rows are k: columns [c0, c0 + 128) of rows k0 .. k0 + 31,
   // `ncols` valid columns, row index mapped through the gather for B in WGRAD
   auto load_t = [&](const uint16_t *M, int64_t ld, int ncols, int c0, int k0, bool gather, SlabT &x) {
-    const int kp = tid & 15, cc = tid >> 4;
-    const int col = c0 + cc * 8;
-    const int k = k0 + 2 * kp;
-    auto row_of = [&](int kk) -> int64_t {
-      if (!gather) return kk;
-      const int p = g.b_gather[kk];
-      return p >= 0 ? p / g.topk : 0;
-    };
-    const bool cin = col < ncols;
-    x.v0 = (cin && k < k_end) ? *reinterpret_cast<const u32x4_t *>(M + row_of(k) * ld + col) : u32x4_t{0, 0, 0, 0};
-    x.v1 = (cin && k + 1 < k_end) ? *reinterpret_cast<const u32x4_t *>(M + row_of(k + 1) * ld + col)
-                                  : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = tid + kThreads * j;
+      const int k = k0 + (c >> 4);
+      const int col = c0 + 8 * (c & 15);
+      int64_t row = k;
+      if (gather && k < k_end) {
+        const int p = g.b_gather[k];
+        row = p >= 0 ? p / g.topk : 0;
+      }
+      x.v[j] = (col < ncols && k < k_end) ? *reinterpret_cast<const u32x4_t *>(M + row * ld + col)
+                                          : u32x4_t{0, 0, 0, 0};
+    }
   };
 
   f32x16_t acc[2][2];
@@ -170,8 +191,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bwd_kernel(BwdGemm g) {
       const int kk = s * 16 + 8 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8_t *>(s_a + (wm * 64 + i * 32 + (lane & 31)) * kLdsRow + kk);
-        bf[i] = *reinterpret_cast<const bf16x8_t *>(s_b + (wn * 64 + i * 32 + (lane & 31)) * kLdsRow + kk);
+        if (MODE == BWD_ROWS)
+          af[i] = *reinterpret_cast<const bf16x8_t *>(s_a + (wm * 64 + i * 32 + (lane & 31)) * kLdsRow + kk);
+        else
+          af[i] = frag_t(s_a, wm * 64 + i * 32, s * 16, lane);
+        bf[i] = frag_t(s_b, wn * 64 + i * 32, s * 16, lane);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
