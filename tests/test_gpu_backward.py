@@ -38,6 +38,16 @@ SHAPES = {
         name="bwd_ragged", T=200, dim=384, n_routed=24, n_groups=1, topk_groups=1, top_k=6,
         n_shared=0, inter_dim=136, score="sigmoid", route_scale=1.5, act="bf16", weight="bf16",
         seed=33, add_residual=0),
+    # one token: K of the E experts get one row each (16-row tiles), the rest nothing
+    "single_token": LayerShape(
+        name="bwd_t1", T=1, dim=256, n_routed=16, n_groups=4, topk_groups=2, top_k=4,
+        n_shared=1, inter_dim=128, score="sigmoid", route_scale=2.5, act="bf16", weight="bf16",
+        seed=35, bias_range=0.1),
+    # ragged T (37): partial dense tiles for the shared expert and the gate
+    "ragged_T37_softmax_norm": LayerShape(
+        name="bwd_t37", T=37, dim=384, n_routed=32, n_groups=1, topk_groups=1, top_k=3,
+        n_shared=2, inter_dim=64, score="softmax", route_scale=1.0, norm_topk=1, act="bf16",
+        weight="bf16", seed=36),
     # Zipf-skewed gate: several experts get no token and must get zero gradients
     "skewed_idle_experts": LayerShape(
         name="bwd_skewed", T=64, dim=256, n_routed=32, n_groups=1, topk_groups=1, top_k=2,
