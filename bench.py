@@ -40,16 +40,16 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_mfma2.hip", "common.hpp"),
-                   "sha256": "6bf092fe7fc2460195aa99bb5c40c866cd37d3ca8d0941d8e66f26abbf8a551b",
-                   "fetch_kib": 8563229, "write_kib": 362496,
+                   "sha256": "d3a9f57ee08f891d67450edaabbc085b569a4a0a170a9014f1f7400dbff71da2",
+                   "fetch_kib": 8591846, "write_kib": 362496,
                    "profile": "profiles/gemm_mfma2_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
-                  "sha256": "4a481e0e556252bf420a7159ff1d6888326a61fd4c1468ad53f555c8d85b3810",
-                  "fetch_kib": 847323, "write_kib": 3744,
+                  "sha256": "6e165d560457fdb1a45f0b781b46aa78408458d359e321cf7b1b92d3c2767d59",
+                  "fetch_kib": 847318, "write_kib": 3744,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
-                "sha256": "0a5337e341a86f335144b52c53da740ae474826da37057f71ce0f3873ca99f95",
-                "fetch_kib": 8186954, "write_kib": 193260,
+                "sha256": "fb510c2673115c68951939bf1e7f7e21d18bc59da417b2804986156d2a1ebdd3",
+                "fetch_kib": 8156458, "write_kib": 193648,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
 }
 
