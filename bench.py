@@ -40,16 +40,16 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_mfma2.hip", "common.hpp"),
-                   "sha256": "d3a9f57ee08f891d67450edaabbc085b569a4a0a170a9014f1f7400dbff71da2",
-                   "fetch_kib": 8591846, "write_kib": 362496,
+                   "sha256": "d70472491b25ea672f17ab25a0ee014e1c9a4b5755a234a21705e0d74a7e32d9",
+                   "fetch_kib": 8574502, "write_kib": 362496,
                    "profile": "profiles/gemm_mfma2_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
-                  "sha256": "6e165d560457fdb1a45f0b781b46aa78408458d359e321cf7b1b92d3c2767d59",
-                  "fetch_kib": 847318, "write_kib": 3744,
+                  "sha256": "0548da35aeff228aa61ccb989c800ae050e479c7221f8bf67360b20f08920222",
+                  "fetch_kib": 847319, "write_kib": 3744,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
-                "sha256": "fb510c2673115c68951939bf1e7f7e21d18bc59da417b2804986156d2a1ebdd3",
-                "fetch_kib": 8156458, "write_kib": 193648,
+                "sha256": "1c09fa9c2fb2b61d75ddc28ee88847b1fa247a64705642e2ba7686184ae8bd8e",
+                "fetch_kib": 8298203, "write_kib": 193809,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
 }
 

@@ -19,8 +19,10 @@
  *    are row-major and dense; "K-contiguous" means the last dimension is the
  *    reduction dimension.
  *  - The caller owns every buffer.  Inputs are read only; outputs are fully
- *    overwritten.  The library allocates no device memory and keeps no mutable
- *    global state, so calls on different streams are independent.
+ *    overwritten.  The library allocates no device memory; its only global
+ *    state is a per-device cache of device properties and kernel attributes,
+ *    filled on first use with atomics, so calls from several threads or on
+ *    different streams and devices are independent.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls only enqueue work: results are ready when the stream is
  *    synchronised.  Nothing is read back to the host.

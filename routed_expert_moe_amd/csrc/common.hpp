@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe355.h"
 
 namespace moe {
@@ -31,6 +33,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
+}
+
+// ---- host-side caches of device properties and kernel attributes --------------
+// One entry per GPU (the current device at the call), filled on first use; the
+// entries are atomics, so concurrent calls from several threads are safe.
+constexpr int kMaxDevices = 64;
+inline int current_device() {
+  int d = 0;
+  return hipGetDevice(&d) == hipSuccess ? d : 0;
+}
+// compute units of the current device
+inline int device_cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  const int d = current_device();
+  int n = d < kMaxDevices ? cache[d].load(std::memory_order_relaxed) : 0;
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess || n <= 0) n = 256;
+  if (d < kMaxDevices) cache[d].store(n, std::memory_order_relaxed);
+  return n;
+}
+// raise a kernel's dynamic LDS limit once per device; `done` is that kernel's bit mask
+inline hipError_t ensure_dynamic_lds(const void *fn, int bytes, std::atomic<uint64_t> &done) {
+  const int d = current_device();
+  const uint64_t bit = d < 64 ? (1ull << d) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 // ---- GEMM segment: C[rows, N] (+)= A[rows, K] * B[N, K]^T for one group of rows

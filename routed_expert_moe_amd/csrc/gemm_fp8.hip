@@ -369,26 +369,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
 
 template <int EPI>
 hipError_t launch_one(const WorkF8 &wk, int grid, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_fp8_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&gemm_fp8_kernel<EPI>), kLdsBytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_fp8_kernel<EPI>), dim3(grid), dim3(kThreads), kLdsBytes, st, wk);
   return hipGetLastError();
-}
-
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
 }
 
 // ---- activation quantisation: 16 lanes per 128-column run (8 values each, one
@@ -455,7 +440,7 @@ hipError_t launch_gemm_fp8(const Segment *segs, int nseg, Epilogue epi, hipStrea
   }
   if (cap == 0) return hipSuccess;
   if (cap >= (1ll << 31)) return hipErrorInvalidValue;
-  int grid = cu_count() / kXcds * kXcds;
+  int grid = device_cu_count() / kXcds * kXcds;
   if (grid < kXcds) grid = kXcds;
   if (epi == EPI_SWIGLU) return launch_one<EPI_SWIGLU>(wk, grid, st);
   return launch_one<EPI_STORE>(wk, grid, st);

@@ -252,17 +252,6 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(Work wk) {
   }
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 }  // namespace
 
 hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool w_fp8,
@@ -283,12 +272,17 @@ hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool 
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
-    return static_cast<int64_t>(cu_count()) * per_cu;
+    return static_cast<int64_t>(device_cu_count()) * per_cu;
   };
 #define MOE_SKINNY(E_, F_, O_)                                                                  \
   do {                                                                                          \
-    static int64_t max_blocks = 0;                                                              \
-    if (max_blocks == 0) max_blocks = resident(reinterpret_cast<const void *>(&gemm_skinny_kernel<E_, F_, O_>)); \
+    static std::atomic<int64_t> resident_cache[kMaxDevices];                                    \
+    const int dev_ = current_device();                                                          \
+    int64_t max_blocks = dev_ < kMaxDevices ? resident_cache[dev_].load(std::memory_order_relaxed) : 0; \
+    if (max_blocks == 0) {                                                                      \
+      max_blocks = resident(reinterpret_cast<const void *>(&gemm_skinny_kernel<E_, F_, O_>));   \
+      if (dev_ < kMaxDevices) resident_cache[dev_].store(max_blocks, std::memory_order_relaxed); \
+    }                                                                                           \
     const dim3 grid(static_cast<unsigned>(blocks < max_blocks ? blocks : max_blocks)), block(kThreads); \
     hipLaunchKernelGGL((gemm_skinny_kernel<E_, F_, O_>), grid, block, 0, st, wk);                 \
   } while (0)
