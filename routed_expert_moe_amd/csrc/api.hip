@@ -741,6 +741,9 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     MOE_NEED(g->dsw13, "grads->dsw13");
     MOE_NEED(g->dsw2, "grads->dsw2");
   }
+  if ((reinterpret_cast<uintptr_t>(topk_idx) | reinterpret_cast<uintptr_t>(topk_w) |
+       reinterpret_cast<uintptr_t>(logits)) % 4 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx, topk_w and logits must be 4-byte aligned");
   const void *vec[] = {x, w->w_gate, w->w13, w->w2, y_pairs, dout, g->dx, g->dw_gate, g->dw13, g->dw2};
   for (const void *q : vec)
     if (!aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "x, weights, y_pairs, dout and the gradients must be 16-byte aligned");

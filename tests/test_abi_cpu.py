@@ -201,6 +201,8 @@ def test_backward_validates_before_launch():
     assert call(wsp=ws + 64) == B.MOE_ERR_INVALID_ARG
     assert call(nb=need - 1) == B.MOE_ERR_WORKSPACE
     assert call(dout=fake + 8) == B.MOE_ERR_INVALID_ARG                    # 16-byte alignment
+    assert L.moe_backward(ctypes.byref(c), T, fake, ctypes.byref(w), ctypes.byref(r), fake + 2, fake, fake,
+                          fake, fake, ctypes.byref(g), ws, need, None) == B.MOE_ERR_INVALID_ARG   # misaligned topk_idx
     for bad in (B.config_of(configs.TINY_F32), B.config_of(configs.V3_DECODE_FP8)):
         with pytest.raises(B.MoeError) as ei:
             B.moe_backward_workspace_size(bad, 8)
