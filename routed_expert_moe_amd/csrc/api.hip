@@ -255,6 +255,7 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
   up[0].a = x;
   up[0].lda = D;
   up[0].gather = r.sorted_pair;
+  up[0].row_pair = r.sorted_pair;
   up[0].topk = c.top_k;
   up[0].b = w.w13;
   up[0].b_stride = 2 * I * D;
@@ -285,6 +286,7 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
   dn[0].expert_off = r.expert_off;
   dn[0].n_tiles_dev = r.n_tiles;
   dn[0].n_tiles_host = r.max_tiles;
+  dn[0].row_pair = r.sorted_pair;
 
   int nseg = 1;
   if (shared) {
@@ -784,6 +786,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   up[0].a = x;
   up[0].lda = D;
   up[0].gather = r->sorted_pair;
+  up[0].row_pair = r->sorted_pair;
   up[0].topk = c.top_k;
   up[0].b = w->w13;
   up[0].b_stride = 2 * I * D;

@@ -93,6 +93,7 @@ struct Segment {
   const int32_t *expert_off;   // first row of each expert, multiples of tile_m (routed only)
   const int32_t *n_tiles_dev;  // nullptr -> dense
   int32_t n_tiles_host;        // dense tile count, or capacity for routed
+  const int32_t *row_pair;     // routed rows' sorted_pair (< 0 marks padding), or nullptr
 };
 
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1 };
