@@ -383,7 +383,7 @@ moe_status check_weights(const moe_config &c, const moe_weights *w, bool need_sh
 struct BwdLayout {
   RoutingLayout rl;
   int64_t tcap;   // 128-row tile capacity
-  size_t off_trow, off_texp, off_tend, off_nt, off_ab, off_dy, off_dh, off_h, off_dab, off_dxp, off_dw,
+  size_t off_trow, off_texp, off_tend, off_tfirst, off_nt, off_ab, off_dy, off_dh, off_h, off_dab, off_dxp, off_dw,
       off_dl, off_dxg, off_abs, off_dhs, off_hsb, off_dabs, off_dxs, total;
 };
 
@@ -402,6 +402,7 @@ BwdLayout bwd_layout(const moe_config &c, int64_t T) {
   L.off_trow = take(4 * static_cast<size_t>(L.tcap));
   L.off_texp = take(4 * static_cast<size_t>(L.tcap));
   L.off_tend = take(4 * static_cast<size_t>(L.tcap));
+  L.off_tfirst = take(4 * static_cast<size_t>(L.tcap));
   L.off_nt = take(4);
   L.off_ab = take(4 * MR * 2 * I);
   L.off_dy = take(2 * MR * D);
@@ -427,6 +428,35 @@ moe_status check_bwd_cfg(const moe_config &c) {
   if (c.dim % 8 || c.inter_dim % 8 || c.n_routed % 8)
     return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs dim, inter_dim and n_routed multiples of 8");
   return MOE_OK;
+}
+
+// Row-form backward product C[rows, n] (fp32) = A[rows, k] B_e[k, n]: on the
+// prefill GEMM's k-strided mode where its tiling fits (K a multiple of 64,
+// routed rows in 128-row routing tiles), else on the backward GEMM
+hipError_t rows_gemm(const BwdGemm &q, const moe_routing *routed, hipStream_t st) {
+  Segment s{};
+  s.a = q.a;
+  s.lda = q.lda;
+  s.b = q.b;
+  s.b_stride = q.b_estride;
+  s.ldb = q.ldb;
+  s.n = q.n;
+  s.k = q.k;
+  s.c = q.c;
+  s.ldc = q.ldc;
+  if (routed != nullptr) {
+    s.tile_row = routed->tile_row;
+    s.tile_expert = routed->tile_expert;
+    s.expert_off = routed->expert_off;
+    s.n_tiles_dev = routed->n_tiles;
+    s.n_tiles_host = routed->max_tiles;
+    s.row_pair = routed->sorted_pair;
+  } else {
+    s.a_rows = q.dense_rows;
+    s.n_tiles_host = (q.dense_rows + 127) / 128;
+  }
+  const bool fits = (routed == nullptr || routed->tile_m == 128) && gemm_mfma2_bt_supported(&s, 1);
+  return fits ? launch_gemm_mfma2_bt(&s, 1, st) : launch_gemm_bwd(q, 1, st);
 }
 
 // C = A B^T with fp32 output (EPI_STORE) on the forward GEMM the plan picks
@@ -766,7 +796,8 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim,
                 E = c.n_routed, K = c.top_k;
   int32_t *trow = static_cast<int32_t *>(at(L.off_trow)), *texp = static_cast<int32_t *>(at(L.off_texp)),
-          *tend = static_cast<int32_t *>(at(L.off_tend)), *nt = static_cast<int32_t *>(at(L.off_nt));
+          *tend = static_cast<int32_t *>(at(L.off_tend)), *tfirst = static_cast<int32_t *>(at(L.off_tfirst)),
+          *nt = static_cast<int32_t *>(at(L.off_nt));
   float *ab = static_cast<float *>(at(L.off_ab)), *dh = static_cast<float *>(at(L.off_dh)),
         *dxp = static_cast<float *>(at(L.off_dxp)), *dw = static_cast<float *>(at(L.off_dw)),
         *dxg = static_cast<float *>(at(L.off_dxg)), *abs_ = static_cast<float *>(at(L.off_abs)),
@@ -813,7 +844,8 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     up[1].n_tiles_host = static_cast<int32_t>((T + p.tile_m - 1) / p.tile_m);
   }
   MOE_BWD(store_gemm_f32(p, up, nseg, st), "backward gate/up recompute launch");
-  MOE_BWD(launch_bwd_tiles(r->expert_off, c.n_routed, trow, texp, tend, nt, st), "backward tile list launch");
+  MOE_BWD(launch_bwd_tiles(r->expert_off, c.n_routed, trow, texp, tend, tfirst, nt, st),
+          "backward tile list launch");
 
   // 2. combine: dw, dy
   MOE_BWD(launch_combine_bwd(dout, y_pairs, *r, topk_w, c.top_k, c.dim, dy, dw, st), "combine backward launch");
@@ -824,6 +856,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   rg.tile_row = trow;
   rg.tile_expert = texp;
   rg.tile_end = tend;
+  rg.tile_first = tfirst;
   rg.n_tiles_dev = nt;
   rg.n_tiles_host = static_cast<int32_t>(L.tcap);
   BwdGemm q = rg;
@@ -836,7 +869,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   q.ldc = I;
   q.n = static_cast<int32_t>(I);
   q.k = static_cast<int32_t>(D);
-  MOE_BWD(launch_gemm_bwd(q, 1, st), "backward dh launch");
+  MOE_BWD(rows_gemm(q, r, st), "backward dh launch");
   MOE_BWD(launch_swiglu_bwd(ab, dh, r->n_tiles, r->tile_m, r->max_rows, static_cast<int>(I), hb, dab, st),
           "backward SwiGLU launch");
   q = rg;
@@ -849,7 +882,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   q.ldc = D;
   q.n = static_cast<int32_t>(D);
   q.k = static_cast<int32_t>(2 * I);
-  MOE_BWD(launch_gemm_bwd(q, 1, st), "backward dx launch");
+  MOE_BWD(rows_gemm(q, r, st), "backward dx launch");
   BwdGemm wg{};
   wg.mode = BWD_WGRAD;
   wg.expert_off = r->expert_off;
@@ -892,7 +925,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     q.ldc = SI;
     q.n = static_cast<int32_t>(SI);
     q.k = static_cast<int32_t>(D);
-    MOE_BWD(launch_gemm_bwd(q, 1, st), "backward shared dh launch");
+    MOE_BWD(rows_gemm(q, nullptr, st), "backward shared dh launch");
     MOE_BWD(launch_swiglu_bwd(abs_, dhs, nullptr, 0, T, static_cast<int>(SI), hsb, dabs, st),
             "backward shared SwiGLU launch");
     q = dg;
@@ -904,7 +937,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     q.ldc = D;
     q.n = static_cast<int32_t>(D);
     q.k = static_cast<int32_t>(2 * SI);
-    MOE_BWD(launch_gemm_bwd(q, 1, st), "backward shared dx launch");
+    MOE_BWD(rows_gemm(q, nullptr, st), "backward shared dx launch");
     BwdGemm dw1{};
     dw1.mode = BWD_WGRAD;
     dw1.dense_rows = static_cast<int32_t>(T);
@@ -944,7 +977,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     dg.ldc = D;
     dg.n = static_cast<int32_t>(D);
     dg.k = static_cast<int32_t>(E);
-    MOE_BWD(launch_gemm_bwd(dg, 1, st), "gate dx launch");
+    MOE_BWD(rows_gemm(dg, nullptr, st), "gate dx launch");
     BwdGemm gw{};
     gw.mode = BWD_WGRAD;
     gw.dense_rows = static_cast<int32_t>(T);

@@ -41,15 +41,18 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // 128-row tiles over each expert's rows [off[e], off[e+1]) (one thread)
 __global__ void bwd_tiles_kernel(const int32_t *__restrict__ expert_off, int E, int32_t *tile_row,
-                                 int32_t *tile_expert, int32_t *tile_end, int32_t *n_tiles) {
+                                 int32_t *tile_expert, int32_t *tile_end, int32_t *tile_first,
+                                 int32_t *n_tiles) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int n = 0;
   for (int e = 0; e < E; ++e) {
     const int a = expert_off[e], b = expert_off[e + 1];
+    const int first = n;
     for (int r = a; r < b; r += 128) {
       tile_row[n] = r;
       tile_expert[n] = e;
       tile_end[n] = b;
+      tile_first[n] = first;
       ++n;
     }
   }
@@ -207,9 +210,9 @@ __global__ __launch_bounds__(256) void dx_final_kernel(
 }  // namespace
 
 hipError_t launch_bwd_tiles(const int32_t *expert_off, int E, int32_t *tile_row, int32_t *tile_expert,
-                            int32_t *tile_end, int32_t *n_tiles, hipStream_t st) {
+                            int32_t *tile_end, int32_t *tile_first, int32_t *n_tiles, hipStream_t st) {
   hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(64), 0, st, expert_off, E, tile_row, tile_expert,
-                     tile_end, n_tiles);
+                     tile_end, tile_first, n_tiles);
   return hipGetLastError();
 }
 

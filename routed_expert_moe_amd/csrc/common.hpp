@@ -94,6 +94,7 @@ struct Segment {
   const int32_t *n_tiles_dev;  // nullptr -> dense
   int32_t n_tiles_host;        // dense tile count, or capacity for routed
   const int32_t *row_pair;     // routed rows' sorted_pair (< 0 marks padding), or nullptr
+  int64_t ldb;                 // k-strided B (backward row form): elements per B row
 };
 
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1 };
@@ -119,13 +120,14 @@ struct BwdGemm {
   int64_t c_estride;            // WGRAD: elements between experts' C
   int32_t m, n, k;              // ROWS: n, k; WGRAD: m, n
   const int32_t *tile_row, *tile_expert, *tile_end, *n_tiles_dev;   // ROWS routed
+  const int32_t *tile_first;    // ROWS routed: index of the first tile of each tile's expert
   int32_t n_tiles_host;         // ROWS routed: tile capacity
   int32_t dense_rows;           // dense segment rows (ROWS tiles / WGRAD reduction)
   const int32_t *expert_off;    // WGRAD routed
 };
 hipError_t launch_gemm_bwd(const BwdGemm &g, int groups, hipStream_t st);
 hipError_t launch_bwd_tiles(const int32_t *expert_off, int E, int32_t *tile_row, int32_t *tile_expert,
-                            int32_t *tile_end, int32_t *n_tiles, hipStream_t st);
+                            int32_t *tile_end, int32_t *tile_first, int32_t *n_tiles, hipStream_t st);
 hipError_t launch_combine_bwd(const void *dout, const void *y, const moe_routing &r, const float *topk_w,
                               int K, int D, void *dy, float *dw, hipStream_t st);
 hipError_t launch_swiglu_bwd(const float *ab, const float *dh, const int32_t *n_tiles, int tile_m,
@@ -175,6 +177,10 @@ hipError_t launch_gemm_mfma(const Segment *segs, int nseg, int tile_m, Epilogue 
 bool gemm_mfma2_supported(const Segment *segs, int nseg);
 hipError_t launch_gemm_mfma2(const Segment *segs, int nseg, Epilogue epi, bool out_f32,
                              hipStream_t st);
+// C[rows, n] (fp32) = A[rows, k] B_e[k, n] with B_e stored [k][n] (row length n),
+// on the prefill GEMM's tiling; routed segments need 128-row routing tiles
+bool gemm_mfma2_bt_supported(const Segment *segs, int nseg);
+hipError_t launch_gemm_mfma2_bt(const Segment *segs, int nseg, hipStream_t st);
 hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool w_fp8,
                               bool out_f32, hipStream_t st);
 

@@ -15,13 +15,21 @@
 // and load:
 //  * k-contiguous (A in ROWS) as [row][k], rows padded to 80 bytes, so the
 //    16-byte fragment reads of 8 consecutive rows hit distinct banks;
-//  * k-strided (B in ROWS, both in WGRAD) as [k][col], rows padded to 288
+//  * k-strided (B in ROWS, both in WGRAD) as [k][col], rows padded to 320
 //    bytes; an MFMA operand (8 consecutive k of one column per lane) is then
 //    read with two ds_read_b64_tr_b16: within each 16-lane group, lane q
 //    addresses 4 columns of row kb + q/4 and lane l receives column l of rows
-//    kb .. kb+3 (the padding puts the four rows' 32-byte pieces on distinct
-//    banks).
+//    kb .. kb+3.  The LDS serves these 8-byte reads 32 lanes at a time: four
+//    rows x 64 bytes, which a row stride of 256 + 64 bytes puts on four
+//    disjoint 16-bank ranges (a 288-byte stride overlapped them, and LDS bank
+//    conflicts took a third of the LDS cycles).
 // The next step's global loads are issued before the current step's MFMAs.
+//
+// ROWS block order: workgroup b runs on XCD b % 8, so each XCD is given a
+// contiguous range of the work list, and inside each run of up to eight
+// M-tiles of one expert the list goes column block by column block: the tiles
+// that read one column block of the expert's B run side by side on one XCD and
+// share it through L2 (in tile-major order each tile streamed the whole B).
 //
 // Rows past a tile's end are read (clamped to a valid row) but never stored; a
 // WGRAD segment with no rows stores zeros.  Requires every k-contiguous extent
@@ -33,9 +41,11 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+constexpr int kGroup = 8;                    // M-tiles of one expert whose blocks interleave (ROWS)
 constexpr int kLdsRow = 40;                  // [row][k] tile: bf16 per row (32 + 8 pad = 80 bytes)
 constexpr int kTileElems = 128 * kLdsRow;
-constexpr int kTRow = 144;                   // [k][col] tile: bf16 per row (128 + 16 pad = 288 bytes)
+constexpr int kTRow = 160;                   // [k][col] tile: bf16 per row (128 + 32 pad = 320 bytes)
 constexpr int kTTileElems = BK * kTRow;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -95,10 +105,29 @@ __global__ __launch_bounds__(kThreads) void gemm_bwd_kernel(BwdGemm g) {
   int m0, n0, row_end = 0, k_begin, k_end, e = 0;
   if (MODE == BWD_ROWS) {
     const int nbn = (g.n + BN - 1) / BN;
-    const int ti = blockIdx.x / nbn;
-    n0 = (blockIdx.x - ti * nbn) * BN;
     const int ntiles = g.n_tiles_dev ? *g.n_tiles_dev : (g.dense_rows + BM - 1) / BM;
-    if (ti >= ntiles) return;
+    // the grid covers the tile capacity in a multiple of 8 blocks; XCD b % 8 takes
+    // the contiguous range [xcd * per, xcd * per + per) of the ntiles * nbn items
+    const int per = (ntiles * nbn + kXcds - 1) / kXcds;
+    const int slot_x = blockIdx.x / kXcds;
+    if (slot_x >= per) return;
+    const int item = (blockIdx.x % kXcds) * per + slot_x;
+    const int slot = item / nbn;
+    if (slot >= ntiles) return;
+    int first, last;
+    if (g.n_tiles_dev) {
+      first = g.tile_first[slot];
+      last = first + (g.tile_end[slot] - g.tile_row[first] + BM - 1) / BM;
+    } else {
+      first = 0;
+      last = ntiles;
+    }
+    const int g0 = first + (slot - first) / kGroup * kGroup;
+    const int gs = min(kGroup, last - g0);
+    const int lg = item - g0 * nbn;
+    const int nbi = lg / gs;
+    const int ti = g0 + lg - nbi * gs;
+    n0 = nbi * BN;
     if (g.n_tiles_dev) {
       m0 = g.tile_row[ti];
       e = g.tile_expert[ti];
@@ -228,7 +257,7 @@ hipError_t launch_gemm_bwd(const BwdGemm &g, int groups, hipStream_t st) {
   if (g.mode == BWD_ROWS) {
     const int nbn = (g.n + BN - 1) / BN;
     const int64_t tiles = g.n_tiles_dev ? g.n_tiles_host : (g.dense_rows + BM - 1) / BM;
-    const int64_t blocks = tiles * nbn;
+    const int64_t blocks = (tiles * nbn + kXcds - 1) / kXcds * kXcds;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(gemm_bwd_kernel<BWD_ROWS>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, g);
   } else {

@@ -15,11 +15,15 @@
 // multiplies it by c_{b-1} / c_b before the block's MFMAs, and the epilogue
 // multiplies by the last c.  That is exact up to one fp32 rounding per block.
 //
+// Routed tiles skip the MFMAs, fragment reads and rescaling of 32-row blocks
+// that hold only padding (an expert's last tile); those rows come out as zeros.
+//
 // Epilogues: EPI_STORE rounds to bf16 (the down projection); EPI_SWIGLU forms
 // silu(gate) * up in fp32, stages the 128 x 256 tile in LDS and quantises every
 // 128-column run of a row to e4m3 with s = max|h| / 448 (1 for a zero run),
 // code = RNE(h / s), writing codes and scales.
 #include "common.hpp"
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -219,61 +223,86 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
       return v;
     };
 
-    // branch-free K loop: block 0's scales seed c_prev (the first rescale multiplies
-    // zeros by one), and the last step prefetches block nk-1 again into the stage
-    // its predecessor has finished with
-    float sa[4], c_prev[4][NJ];
+    // 32-row blocks of this tile that hold real rows (routed padding, sorted_pair < 0,
+    // sits at the end of an expert's last tile)
+    int nblk = 4;
+    if (sg.row_pair != nullptr) {
+      nblk = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = ascale(i, 0);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const float sw0 = wscale(j, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c_prev[i][j] = sa[i] * sw0;
+      for (int i = 0; i < 4; ++i) nblk += sg.row_pair[row0 + 32 * i] >= 0 ? 1 : 0;
+    } else if (dense) {
+      nblk = min(4, (sg.a_rows - row0 + 31) / 32);
     }
-    issue(0);
-    for (int kt = 0; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // this step's tiles (and its scales) have landed
-      __builtin_amdgcn_s_barrier();
-      const char *st = lds + (kt & 1) * kStageBytes;
-      const int kn = min(kt + 1, nk - 1);
-      // next block's activation scales first, then its tiles: waiting for the
-      // scales (older in the in-order queue) never waits for the tiles
-      float sa_next[4];
+    nblk = uniform(nblk);
+
+    float sa[4], c_prev[4][NJ];
+    auto kloop = [&](auto nbc) {
+      constexpr int NB = decltype(nbc)::value;
+      // branch-free K loop: block 0's scales seed c_prev (the first rescale multiplies
+      // zeros by one), and the last step prefetches block nk-1 again into the stage
+      // its predecessor has finished with
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa_next[i] = ascale(i, kn);
-      issue(kn);
-      // rescale the running sums from block kt-1's scale to block kt's
+      for (int i = 0; i < 4; ++i) sa[i] = ascale(i, 0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const float sw = wscale(j, kt);
+        const float sw0 = wscale(j, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float c = sa[i] * sw;
-          const float ratio = c_prev[i][j] * __builtin_amdgcn_rcpf(c);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] *= ratio;
-          c_prev[i][j] = c;
-        }
+        for (int i = 0; i < 4; ++i) c_prev[i][j] = sa[i] * sw0;
       }
+      issue(0);
+      for (int kt = 0; kt < nk; ++kt) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // this step's tiles (and its scales) have landed
+        __builtin_amdgcn_s_barrier();
+        const char *st = lds + (kt & 1) * kStageBytes;
+        const int kn = min(kt + 1, nk - 1);
+        // next block's activation scales first, then its tiles: waiting for the
+        // scales (older in the in-order queue) never waits for the tiles
+        float sa_next[4];
 #pragma unroll
-      for (int s = 0; s < BK / 64; ++s) {
-        v8i_t bf[NJ];
+        for (int i = 0; i < 4; ++i) sa_next[i] = ascale(i, kn);
+        issue(kn);
+        // rescale the running sums from block kt-1's scale to block kt's
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) bf[j] = read_frag(st + kATileBytes, brow_l[j], s);
+        for (int j = 0; j < NJ; ++j) {
+          const float sw = wscale(j, kt);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v8i_t af = read_frag(st, i * 32 + l32, s);
+          for (int i = 0; i < 4; ++i) {
+            const float c = sa[i] * sw;
+            if (i >= NB) {   // padding block: keep the scale bookkeeping only
+              c_prev[i][j] = c;
+              continue;
+            }
+            const float ratio = c_prev[i][j] * __builtin_amdgcn_rcpf(c);
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)   // weight fragment first: lanes end with 4 consecutive columns
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
-                                                                         127, 0, 127);
+            for (int r = 0; r < 16; ++r) acc[i][j][r] *= ratio;
+            c_prev[i][j] = c;
+          }
         }
-        // one slice's fragments at a time (hoisting both slices' reads runs out of registers)
-        __builtin_amdgcn_sched_barrier(0);
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = sa_next[i];
+        for (int s = 0; s < BK / 64; ++s) {
+          v8i_t bf[NJ];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) bf[j] = read_frag(st + kATileBytes, brow_l[j], s);
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            const v8i_t af = read_frag(st, i * 32 + l32, s);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)   // weight fragment first: lanes end with 4 consecutive columns
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
+                                                                           127, 0, 127);
+          }
+          // one slice's fragments at a time (hoisting both slices' reads runs out of registers)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = sa_next[i];
+      }
+    };
+    switch (nblk) {
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      default: kloop(std::integral_constant<int, 4>{}); break;
     }
     __syncthreads();   // all waves done with both stages
 

@@ -32,6 +32,16 @@
 // and the block comes from HBM once; in tile-major order an expert's tiles
 // often landed in different rounds and each re-read the weights.
 //
+// Two operand layouts:
+//   NT  C = A B_e^T, both k-contiguous (the forward).
+//   NN  C = A B_e with B_e stored [k][n] (the backward's row-form products):
+//       each K step stages 64 k-rows of 512 columns as 1 KiB LDS rows.
+// The k-strided tile stores the 64-byte block b of k-row r at block b ^ (r & 3)
+// and its MFMA operand (8 consecutive k of one column per lane) is read with
+// two ds_read_b64_tr_b16.  The LDS serves those 8-byte reads 32 lanes at a
+// time, four k-rows x 64 bytes, which the swizzle puts on four disjoint bank
+// ranges.
+//
 // Routed tiles skip the MFMAs and fragment reads of 32-row blocks that hold
 // only padding (an expert's last tile): on a 256-expert, top-8 routing of 8192
 // tokens that is 15% of the routed MFMA work.  Skipped blocks store zeros.
@@ -64,6 +74,8 @@ constexpr int kBLoads = BN * kRowBytes / 1024 / kWaves;  // wave loads of B per 
 constexpr int kLoads = kALoads + kBLoads;                // per wavefront per K step
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
 struct Work2 {
@@ -83,7 +95,35 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-template <int EPI, bool OUT_F32>
+// two 4 x bf16 transposed reads -> one MFMA operand of 8 bf16
+__device__ __forceinline__ bf16x8_t join_tr(v4i16_t lo, v4i16_t hi) {
+  const u32x4_t v = {static_cast<uint32_t>(static_cast<uint16_t>(lo[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[1])) << 16),
+                     static_cast<uint32_t>(static_cast<uint16_t>(lo[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[3])) << 16),
+                     static_cast<uint32_t>(static_cast<uint16_t>(hi[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[1])) << 16),
+                     static_cast<uint32_t>(static_cast<uint16_t>(hi[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[3])) << 16)};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+constexpr int kLayNT = 0, kLayNN = 1;
+
+// byte offset of (k-row r, tile column c) in a k-strided stage of ROW-byte rows
+template <int ROW>
+__device__ __forceinline__ int kt_off(int r, int c) { return r * ROW + (((c >> 5) ^ (r & 3)) << 6) + ((c * 2) & 63); }
+
+// MFMA operand of tile columns [cb, cb + 32), K slice s from a k-strided stage:
+// lane 16g + q addresses k-row kr + q/4, columns cb + 16(g&1) + 4(q%4); lane
+// 16g + l receives column cb + 16(g&1) + l of k-rows kr .. kr+3, then kr+4 .. kr+7
+template <int ROW>
+__device__ __forceinline__ bf16x8_t frag_kt(const char *base, int cb, int s, int lane) {
+  const int g = lane >> 4, q = lane & 15;
+  const int kr = 16 * s + 8 * (g >> 1) + (q >> 2);
+  const int col = cb + 16 * (g & 1) + 4 * (q & 3);
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(base + kt_off<ROW>(kr, col)));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(base + kt_off<ROW>(kr + 4, col)));
+  return join_tr(lo, hi);
+}
+
+template <int EPI, bool OUT_F32, int LAY>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
@@ -153,7 +193,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
       asrc[i] = A + arow * sg.lda + (pch ^ swz(r)) * 8;
     }
     const uint16_t *Bm = static_cast<const uint16_t *>(sg.b) + static_cast<int64_t>(expert) * sg.b_stride;
-    auto bptr = [&](int i) -> const uint16_t * {
+    auto bptr = [&](int i, int kt) -> const uint16_t * {
+      if (LAY == kLayNN) {   // k-row kr of the step; this lane fills physical 16-byte chunk `lane` of its LDS row
+        const int kr = wave * kBLoads + i;
+        int col = nb * BN + ((((lane >> 2) ^ (kr & 3)) << 5) | ((lane & 3) << 3));
+        if (col > sg.n - 8) col = sg.n - 8;
+        return Bm + static_cast<int64_t>(kt * BK + kr) * sg.ldb + col;
+      }
       const int r = (wave * kBLoads + i) * 8 + lrow;    // B tile row
       int brow;
       if (EPI == EPI_SWIGLU) {
@@ -164,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
         brow = nb * BN + r;
         if (brow >= sg.n) brow = sg.n - 1;
       }
-      return Bm + static_cast<int64_t>(brow) * K + (pch ^ swz(r)) * 8;
+      return Bm + static_cast<int64_t>(brow) * K + (pch ^ swz(r)) * 8 + kt * BK;
     };
     auto issue_one = [&](int li, int kt) {
       char *st = lds + (kt & 1) * kStageBytes;
@@ -172,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
       if (li < kALoads)
         load_lds16(asrc[li] + k0, st + (wave * kALoads + li) * 1024);
       else
-        load_lds16(bptr(li - kALoads) + k0, st + kATileBytes + (wave * kBLoads + li - kALoads) * 1024);
+        load_lds16(bptr(li - kALoads, kt), st + kATileBytes + (wave * kBLoads + li - kALoads) * 1024);
     };
 
     f32x16_t acc[4][NJ];
@@ -214,10 +260,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
           const int r = i * 32 + l32;
           af[i] = __builtin_bit_cast(bf16x8_t, As[r * 8 + (c ^ swz(r))]);
         }
+        if (LAY == kLayNN) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int r = brow_l[j];
-          bf[j] = __builtin_bit_cast(bf16x8_t, Bs[r * 8 + (c ^ swz(r))]);
+          for (int j = 0; j < NJ; ++j) bf[j] = frag_kt<BN * 2>(st + kATileBytes, brow_l[j] - l32, s, lane);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int r = brow_l[j];
+            bf[j] = __builtin_bit_cast(bf16x8_t, Bs[r * 8 + (c ^ swz(r))]);
+          }
         }
       };
 #pragma unroll
@@ -246,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
         // schedule: the fragment reads of K-slice s+1 go one by one between the MFMAs of
         // slice s, so each wavefront waits on LDS once per slice (left alone, the compiler
         // reused one fragment set and waited every two to four MFMAs)
-        constexpr int NM = NB * NJ, ND = NB + NJ;
+        constexpr int NM = NB * NJ, ND = NB + (LAY == kLayNN ? 2 : 1) * NJ;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
           if (s + 1 < BK / 16) {
@@ -275,6 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
     // 4 consecutive columns as one 8-byte LDS store, then every wavefront writes
     // 1 KiB runs of whole output rows (eight full 128-byte lines per store).
     if (OUT_F32) {
+      float *C = static_cast<float *>(sg.c);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int grow = row0 + i * 32 + l32;
@@ -286,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
             const int col = nb * BN + wave * NJ * 32 + j * 32 + 8 * g + 4 * khalf;
             if (col >= sg.n) continue;
             const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            *reinterpret_cast<f32x4_t *>(static_cast<float *>(sg.c) + static_cast<int64_t>(grow) * sg.ldc + col) = v;
+            *reinterpret_cast<f32x4_t *>(C + static_cast<int64_t>(grow) * sg.ldc + col) = v;
           }
       }
     } else {
@@ -343,12 +395,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
   }
 }
 
-template <int EPI, bool OUT_F32>
+template <int EPI, bool OUT_F32, int LAY = kLayNT>
 hipError_t launch_one(const Work2 &wk, int grid, hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&gemm_mfma2_kernel<EPI, OUT_F32>), kLdsBytes, lds_set);
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&gemm_mfma2_kernel<EPI, OUT_F32, LAY>), kLdsBytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_mfma2_kernel<EPI, OUT_F32>), dim3(grid), dim3(kThreads), kLdsBytes, st, wk);
+  hipLaunchKernelGGL((gemm_mfma2_kernel<EPI, OUT_F32, LAY>), dim3(grid), dim3(kThreads), kLdsBytes, st, wk);
   return hipGetLastError();
 }
 
@@ -360,9 +412,9 @@ bool gemm_mfma2_supported(const Segment *segs, int nseg) {
   return true;
 }
 
-hipError_t launch_gemm_mfma2(const Segment *segs, int nseg, Epilogue epi, bool out_f32,
-                             hipStream_t st) {
-  Work2 wk{};
+namespace {
+// the work list of the segments; returns its capacity in items
+int64_t fill_work(const Segment *segs, int nseg, Epilogue epi, Work2 &wk) {
   wk.nseg = nseg;
   int64_t cap = 0;
   for (int s = 0; s < nseg; ++s) {
@@ -372,13 +424,40 @@ hipError_t launch_gemm_mfma2(const Segment *segs, int nseg, Epilogue epi, bool o
     wk.nblk_n[s] = (ncols + per - 1) / per;
     cap += static_cast<int64_t>(segs[s].n_tiles_host) * wk.nblk_n[s];
   }
+  return cap;
+}
+
+int grid_size() {
+  const int grid = device_cu_count() / kXcds * kXcds;
+  return grid < kXcds ? kXcds : grid;
+}
+}  // namespace
+
+hipError_t launch_gemm_mfma2(const Segment *segs, int nseg, Epilogue epi, bool out_f32,
+                             hipStream_t st) {
+  Work2 wk{};
+  const int64_t cap = fill_work(segs, nseg, epi, wk);
   if (cap == 0) return hipSuccess;
   if (cap >= (1ll << 31)) return hipErrorInvalidValue;
-  int grid = device_cu_count() / kXcds * kXcds;
-  if (grid < kXcds) grid = kXcds;
+  const int grid = grid_size();
   if (epi == EPI_SWIGLU) return launch_one<EPI_SWIGLU, false>(wk, grid, st);
   if (out_f32) return launch_one<EPI_STORE, true>(wk, grid, st);
   return launch_one<EPI_STORE, false>(wk, grid, st);
+}
+
+bool gemm_mfma2_bt_supported(const Segment *segs, int nseg) {
+  for (int s = 0; s < nseg; ++s)
+    if (segs[s].k % BK != 0 || segs[s].k <= 0 || segs[s].n % 8 != 0 || segs[s].n < 8 || segs[s].ldc % 4 != 0)
+      return false;
+  return true;
+}
+
+hipError_t launch_gemm_mfma2_bt(const Segment *segs, int nseg, hipStream_t st) {
+  Work2 wk{};
+  const int64_t cap = fill_work(segs, nseg, EPI_STORE, wk);
+  if (cap == 0) return hipSuccess;
+  if (cap >= (1ll << 31)) return hipErrorInvalidValue;
+  return launch_one<EPI_STORE, true, kLayNN>(wk, grid_size(), st);
 }
 
 }  // namespace moe
