@@ -6,7 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "common.hpp"
+#include "backward.hpp"
 
 namespace moe {
 int64_t permute_scratch_ints(int64_t P, int E);

@@ -11,7 +11,7 @@
 // Every sum runs in a fixed order; the outputs are the same on every run.
 #include <math.h>
 
-#include "common.hpp"
+#include "backward.hpp"
 
 namespace moe {
 namespace {

@@ -34,7 +34,7 @@
 // Rows past a tile's end are read (clamped to a valid row) but never stored; a
 // WGRAD segment with no rows stores zeros.  Requires every k-contiguous extent
 // and every column count to be a multiple of 8.
-#include "common.hpp"
+#include "backward.hpp"
 
 namespace moe {
 namespace {
