@@ -384,7 +384,7 @@ struct BwdLayout {
   RoutingLayout rl;
   int64_t tcap;   // 128-row tile capacity
   size_t off_trow, off_texp, off_tend, off_tfirst, off_nt, off_ab, off_dy, off_dh, off_h, off_dab, off_dxp, off_dw,
-      off_dl, off_dxg, off_abs, off_dhs, off_hsb, off_dabs, off_dxs, total;
+      off_dl, off_dxg, off_abs, off_dhs, off_hsb, off_dabs, off_dxs, off_xs, total;
 };
 
 BwdLayout bwd_layout(const moe_config &c, int64_t T) {
@@ -418,6 +418,7 @@ BwdLayout bwd_layout(const moe_config &c, int64_t T) {
   L.off_hsb = take(2 * Tz * SI);
   L.off_dabs = take(2 * Tz * 2 * SI);
   L.off_dxs = take(4 * Tz * D);
+  L.off_xs = take(2 * MR * D);
   L.total = o;
   return L;
 }
@@ -803,7 +804,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
         *dxg = static_cast<float *>(at(L.off_dxg)), *abs_ = static_cast<float *>(at(L.off_abs)),
         *dhs = static_cast<float *>(at(L.off_dhs)), *dxs = static_cast<float *>(at(L.off_dxs));
   void *dy = at(L.off_dy), *hb = at(L.off_h), *dab = at(L.off_dab), *dl = at(L.off_dl), *hsb = at(L.off_hsb),
-       *dabs = at(L.off_dabs);
+       *dabs = at(L.off_dabs), *xs = at(L.off_xs);
   auto bf = [](const void *q) { return static_cast<const uint16_t *>(q); };
   hipError_t e = hipSuccess;
 #define MOE_BWD(call, what) \
@@ -897,13 +898,13 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   q.m = static_cast<int32_t>(D);
   q.n = static_cast<int32_t>(I);
   MOE_BWD(launch_gemm_bwd(q, c.n_routed, st), "backward dW2 launch");
+  // dW13_e reads the tokens in routed-row order
+  MOE_BWD(launch_gather_rows(x, *r, c.top_k, c.dim, xs, st), "backward token gather launch");
   q = wg;
   q.a = bf(dab);
   q.lda = 2 * I;
-  q.b = bf(x);
+  q.b = bf(xs);
   q.ldb = D;
-  q.b_gather = r->sorted_pair;
-  q.topk = c.top_k;
   q.c = g->dw13;
   q.ldc = D;
   q.c_estride = 2 * I * D;

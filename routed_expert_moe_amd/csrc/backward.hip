@@ -116,6 +116,25 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
   }
 }
 
+// x in routed-row order: xs[r] = x[token of sorted_pair[r]], zeros for a padding
+// row; one workgroup per used row, 16 bytes per thread
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__restrict__ x,
+                                                          const int32_t *__restrict__ sorted_pair,
+                                                          const int32_t *__restrict__ n_tiles, int tile_m, int K,
+                                                          int D, uint16_t *__restrict__ xs) {
+  const int row = blockIdx.x;
+  if (row >= *n_tiles * tile_m) return;
+  const int p = sorted_pair[row];
+  const int nc = D / 8;
+  u32x4_t *dst = reinterpret_cast<u32x4_t *>(xs + static_cast<int64_t>(row) * D);
+  if (p < 0) {
+    for (int c = threadIdx.x; c < nc; c += 256) dst[c] = u32x4_t{0, 0, 0, 0};
+    return;
+  }
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + static_cast<int64_t>(p / K) * D);
+  for (int c = threadIdx.x; c < nc; c += 256) dst[c] = src[c];
+}
+
 // one wavefront per token
 __global__ __launch_bounds__(64) void gate_bwd_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ pair_row,
@@ -233,6 +252,14 @@ hipError_t launch_swiglu_bwd(const float *ab, const float *dh, const int32_t *n_
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, ab, dh,
                      n_tiles, tile_m, rows_host, I, static_cast<uint16_t *>(h), static_cast<uint16_t *>(dab));
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void *x, const moe_routing &r, int K, int D, void *xs, hipStream_t st) {
+  if (r.max_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(r.max_rows)), dim3(256), 0, st,
+                     static_cast<const uint16_t *>(x), r.sorted_pair, r.n_tiles, r.tile_m, K, D,
+                     static_cast<uint16_t *>(xs));
   return hipGetLastError();
 }
 

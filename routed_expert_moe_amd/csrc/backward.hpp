@@ -7,9 +7,8 @@ namespace moe {
 // ---- backward GEMMs (bf16 operands, fp32 C) --------------------------------
 //   BWD_ROWS:  C[r, n] = sum_k A[r, k] B_e[k, n]; rows r of 128-row tiles (tile
 //              lists from launch_bwd_tiles) or of [0, dense_rows)
-//   BWD_WGRAD: C_e[m, n] = sum_r A[r, m] B[g(r), n]; r over [expert_off[e],
-//              expert_off[e+1]) or [0, dense_rows); g(r) = b_gather[r] / topk
-//              (0 for a padding row) when b_gather is given, else r
+//   BWD_WGRAD: C_e[m, n] = sum_r A[r, m] B[r, n]; r over [expert_off[e],
+//              expert_off[e+1]) or [0, dense_rows)
 enum BwdMode { BWD_ROWS = 0, BWD_WGRAD = 1 };
 struct BwdGemm {
   int32_t mode;
@@ -18,8 +17,6 @@ struct BwdGemm {
   const uint16_t *b;
   int64_t ldb;
   int64_t b_estride;            // ROWS: elements between experts' B
-  const int32_t *b_gather;      // WGRAD: sorted_pair, or nullptr
-  int32_t topk;
   float *c;
   int64_t ldc;
   int64_t c_estride;            // WGRAD: elements between experts' C
@@ -35,6 +32,8 @@ hipError_t launch_bwd_tiles(const int32_t *expert_off, int E, int32_t *tile_row,
                             int32_t *tile_end, int32_t *tile_first, int32_t *n_tiles, hipStream_t st);
 hipError_t launch_combine_bwd(const void *dout, const void *y, const moe_routing &r, const float *topk_w,
                               int K, int D, void *dy, float *dw, hipStream_t st);
+// xs[r] = x[sorted_pair[r] / K] for every used routed row (zeros for padding)
+hipError_t launch_gather_rows(const void *x, const moe_routing &r, int K, int D, void *xs, hipStream_t st);
 hipError_t launch_swiglu_bwd(const float *ab, const float *dh, const int32_t *n_tiles, int tile_m,
                              int64_t rows_host, int I, void *h, void *dab, hipStream_t st);
 hipError_t launch_gate_bwd(const moe_config &cfg, int64_t T, const float *logits, const int32_t *topk_idx,
