@@ -40,16 +40,16 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_mfma2.hip", "common.hpp"),
-                   "sha256": "d70472491b25ea672f17ab25a0ee014e1c9a4b5755a234a21705e0d74a7e32d9",
-                   "fetch_kib": 8574502, "write_kib": 362496,
+                   "sha256": "9dbc4256eef59ff14a3fc76bb0f64344d53f279c588794ff37dd95784abcff81",
+                   "fetch_kib": 10697778, "write_kib": 362496,
                    "profile": "profiles/gemm_mfma2_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
-                  "sha256": "0548da35aeff228aa61ccb989c800ae050e479c7221f8bf67360b20f08920222",
-                  "fetch_kib": 847319, "write_kib": 3744,
+                  "sha256": "59dfca776df8586e4571956ac60856b9efcde10db974a41401e24df0a446861b",
+                  "fetch_kib": 847315, "write_kib": 3744,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
-                "sha256": "1c09fa9c2fb2b61d75ddc28ee88847b1fa247a64705642e2ba7686184ae8bd8e",
-                "fetch_kib": 8298203, "write_kib": 193809,
+                "sha256": "c5818489c1ece2dde52e881ed7511c33516576c68d06cbbbbf1a52b4dd3c85ca",
+                "fetch_kib": 9086898, "write_kib": 195749,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
 }
 
