@@ -42,6 +42,8 @@
 // with ds_read_b64_tr_b16 (conflict-free for the same reason as above).  A
 // step that runs past the group's last row reads clamped rows, and each
 // wavefront zeroes the A rows it loaded beyond the end before the barrier.
+// C is written with non-temporal stores (nothing in the call reads it back;
+// 4% off the V3 backward against plain stores).
 //
 // Rows past a tile's end are read (clamped to a valid row) but never stored; a
 // WGRAD group with no rows stores zeros.  Requires every k-contiguous extent
@@ -368,8 +370,8 @@ __global__ __launch_bounds__(kThreads) void gemm_wgrad_kernel(BwdGemm g) {
       const int lr = it * 8 + (threadIdx.x >> 5), cc = threadIdx.x & 31;
       const int m = m0 + h * 64 + lr, n = n0 + cc * 4;
       if (m < g.m && n < g.n)
-        *reinterpret_cast<f32x4_t *>(C + static_cast<int64_t>(m) * g.ldc + n) =
-            *reinterpret_cast<const f32x4_t *>(wl + lr * SROW + cc * 16);
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t *>(wl + lr * SROW + cc * 16),
+                                    reinterpret_cast<f32x4_t *>(C + static_cast<int64_t>(m) * g.ldc + n));
     }
   }
 }
