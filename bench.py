@@ -282,6 +282,30 @@ def time_backward(p: Pass, shape, calls: int = 3):
     return res
 
 
+def time_ep_shard(args):
+    """One GPU's share of the V3 prefill layer under expert parallelism (32 local
+    experts, the tokens dispatched to them, no shared expert): the same step
+    sequence on that share, without the collectives that would feed it."""
+    import torch
+    from routed_expert_moe_amd import configs, synth
+    shape = configs.V3_EP_SHARD_BF16
+    layer = synth.make_layer(shape, device="cuda")
+    p = Pass(layer)
+    total_ms, up_ms, _ = time_pass(p, args.steps, args.warmup)
+    fig = work_figures(layer, p.r.counts.cpu().numpy())
+    ms = total_ms / args.steps
+    res = {"workload": shape.name, "T": shape.T, "n_routed": shape.n_routed, "top_k": shape.top_k,
+           "what": "one GPU's expert-parallel share of v3_prefill_bf16_T8192 (a local routing of the "
+                   "dispatched tokens stands in for the global gate; no collectives)",
+           "ms_per_step": ms, "pairs": shape.T * shape.top_k, "experts_touched": fig["touched"],
+           "layer_tflops": fig["flops_layer"] / (ms / 1e3) / 1e12,
+           "roofline": roofline(fig["flops_up"], fig["bytes_up"], up_ms, None,
+                                "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")}
+    del p, layer
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(layer, n_tokens: int):
     """The float64 oracle on the first n_tokens tokens of the same workload, on host cores."""
     import numpy as np
@@ -411,6 +435,9 @@ def main():
                              "moe_expert_up (fp8 weight-streaming gate/up + SwiGLU, gemm_skinny_kernel)"),
     }
     del dp, dlayer
+    torch.cuda.empty_cache()
+    progress("timing the expert-parallel share")
+    res["ep_shard"] = time_ep_shard(args)
     if not args.no_cpu_baseline:
         progress("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(layer, args.cpu_tokens)

@@ -88,5 +88,15 @@ V3_PREFILL_W8A8 = LayerShape(
     topk_groups=4, top_k=8, n_shared=1, inter_dim=2048, score=SCORE_SIGMOID,
     route_scale=2.5, act="bf16", weight="fp8", act_quant=1, seed=5, bias_range=0.05)
 
-ALL = [TINY_F32, V2_LITE_BF16, V2_BF16, V3_PREFILL_BF16, V3_DECODE_FP8, V3_PREFILL_W8A8]
+# One GPU's share of the V3 prefill layer under expert parallelism over the 8
+# GPUs of a node (one routing group of 32 experts per GPU): the 8192 tokens'
+# 65536 pairs split eight ways, each token reaching at most 4 GPUs, so a GPU
+# receives about 4096 distinct tokens with 2 of its experts each, 256 rows per
+# expert as in the whole layer.  The shared expert runs on the tokens' home GPU.
+V3_EP_SHARD_BF16 = LayerShape(
+    name="v3_ep_shard_bf16_T4096_E32", T=4096, dim=7168, n_routed=32, n_groups=1,
+    topk_groups=1, top_k=2, n_shared=0, inter_dim=2048, score=SCORE_SIGMOID,
+    route_scale=2.5, act="bf16", weight="bf16", seed=6, bias_range=0.05)
+
+ALL = [TINY_F32, V2_LITE_BF16, V2_BF16, V3_PREFILL_BF16, V3_DECODE_FP8, V3_PREFILL_W8A8, V3_EP_SHARD_BF16]
 BY_NAME = {c.name: c for c in ALL}

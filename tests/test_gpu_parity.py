@@ -52,7 +52,8 @@ SHAPES = {
     "v3_decode_fp8": C.V3_DECODE_FP8,
 }
 # full-size shapes: gate on every token, outputs on a token sample
-LARGE = {"v2_T4096": (C.V2_BF16, 12), "v3_prefill_T8192": (C.V3_PREFILL_BF16, 8)}
+LARGE = {"v2_T4096": (C.V2_BF16, 12), "v3_prefill_T8192": (C.V3_PREFILL_BF16, 8),
+         "v3_ep_shard_T4096": (C.V3_EP_SHARD_BF16, 12)}
 
 _cache = {}
 
