@@ -19,6 +19,15 @@
 // line, and the swizzle sends the 8 rows of each parity to 8 different chunks,
 // so the 16 reads cover all 64 banks once.
 //
+// Each wavefront loads exactly the B rows it multiplies (for SwiGLU its 32
+// gate rows and the 32 matching up rows), so B is private to the wavefront and
+// only A is shared: a step waits for the wavefront's own A loads (issued before
+// its B loads, and vmcnt counts in order), passes the barrier that makes every
+// wavefront's A visible, and only then waits for its own B.  A wavefront whose
+// weight rows come late then stalls alone while its SIMD partner keeps the
+// MFMA busy; waiting for all loads before the barrier made every wavefront of
+// the CU wait for the slowest (8% slower gate/up at V3 prefill).
+//
 // The MFMA takes the weight fragment as its first operand, so each lane ends
 // with four consecutive output columns of one row: one 16-byte store for fp32
 // output, one 8-byte LDS store for bf16 output, which is then written to
@@ -193,6 +202,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
       asrc[i] = A + arow * sg.lda + (pch ^ swz(r)) * 8;
     }
     const uint16_t *Bm = static_cast<const uint16_t *>(sg.b) + static_cast<int64_t>(expert) * sg.b_stride;
+    // first B tile row of this wavefront's load i: the rows it multiplies, so B is
+    // private to the wavefront (SwiGLU: 32 gate rows, then the 32 matching up rows)
+    auto brow0 = [&](int i) -> int {
+      if (EPI == EPI_SWIGLU && LAY == kLayNT)
+        return i < kBLoads / 2 ? wave * (BN / 2 / kWaves) + 8 * i : BN / 2 + wave * (BN / 2 / kWaves) + 8 * (i - kBLoads / 2);
+      return (wave * kBLoads + i) * 8;
+    };
     auto bptr = [&](int i, int kt) -> const uint16_t * {
       if (LAY == kLayNN) {   // k-row kr of the step; this lane fills physical 16-byte chunk `lane` of its LDS row
         const int kr = wave * kBLoads + i;
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
         if (col > sg.n - 8) col = sg.n - 8;
         return Bm + static_cast<int64_t>(kt * BK + kr) * sg.ldb + col;
       }
-      const int r = (wave * kBLoads + i) * 8 + lrow;    // B tile row
+      const int r = brow0(i) + lrow;    // B tile row (the rows this wavefront reads)
       int brow;
       if (EPI == EPI_SWIGLU) {
         const int col = nb * (BN / 2) + (r & (BN / 2 - 1));
@@ -218,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
       if (li < kALoads)
         load_lds16(asrc[li] + k0, st + (wave * kALoads + li) * 1024);
       else
-        load_lds16(bptr(li - kALoads, kt), st + kATileBytes + (wave * kBLoads + li - kALoads) * 1024);
+        load_lds16(bptr(li - kALoads, kt), st + kATileBytes + brow0(li - kALoads) * kRowBytes);
     };
 
     f32x16_t acc[4][NJ];
@@ -274,9 +290,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma2_kernel(Work2 wk) {
 #pragma unroll
       for (int li = 0; li < kLoads; ++li) issue_one(li, 0);
       for (int kt = 0; kt < nk; ++kt) {
-        // stage kt: this wave's loads are the only ones in flight; then a bare barrier
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        // stage kt: this wavefront's A rows (issued before its B rows) have landed;
+        // the barrier makes every wavefront's A rows visible, then its own B rows
+        // (in the k-strided layout every wavefront reads every k-row of B: wait for all)
+        if (LAY == kLayNN) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kBLoads));
         __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         const char *st = lds + (kt & 1) * kStageBytes;
         const bool more = kt + 1 < nk;
         bf16x8_t af[2][NB], bf[2][NJ];
