@@ -40,16 +40,16 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_mfma2.hip", "common.hpp"),
-                   "sha256": "9dbc4256eef59ff14a3fc76bb0f64344d53f279c588794ff37dd95784abcff81",
-                   "fetch_kib": 10382196, "write_kib": 362496,
+                   "sha256": "5ea999a830e876989880a17369a4bd9983bda3dcbcad28bb01a761a5f0239d24",
+                   "fetch_kib": 14221656, "write_kib": 362496,
                    "profile": "profiles/gemm_mfma2_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
                   "sha256": "59dfca776df8586e4571956ac60856b9efcde10db974a41401e24df0a446861b",
-                  "fetch_kib": 847313, "write_kib": 3744,
+                  "fetch_kib": 847312, "write_kib": 3744,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
                 "sha256": "c5818489c1ece2dde52e881ed7511c33516576c68d06cbbbbf1a52b4dd3c85ca",
-                "fetch_kib": 8998258, "write_kib": 196164,
+                "fetch_kib": 9022782, "write_kib": 195868,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
 }
 
