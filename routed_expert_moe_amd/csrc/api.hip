@@ -456,7 +456,9 @@ hipError_t rows_gemm(const BwdGemm &q, const moe_routing *routed, hipStream_t st
     s.a_rows = q.dense_rows;
     s.n_tiles_host = (q.dense_rows + 127) / 128;
   }
-  const bool fits = (routed == nullptr || routed->tile_m == 128) && gemm_mfma2_bt_supported(&s, 1);
+  // 16-byte DMA rows: A and B row lengths multiples of 8 elements
+  const bool fits = (routed == nullptr || routed->tile_m == 128) && q.lda % 8 == 0 && q.ldb % 8 == 0 &&
+                    gemm_mfma2_bt_supported(&s, 1);
   return fits ? launch_gemm_mfma2_bt(&s, 1, st) : launch_gemm_bwd(q, 1, st);
 }
 

@@ -392,7 +392,8 @@ hipError_t launch_gemm_bwd(const BwdGemm &g, int groups, hipStream_t st) {
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(gemm_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, g);
   } else {
-    if (g.m < 8 || g.n < 8) return hipErrorInvalidValue;
+    // 16-byte DMA rows and 16-byte stores of C
+    if (g.m < 8 || g.n < 8 || g.lda % 8 || g.ldb % 8 || g.ldc % 4 || g.c_estride % 4) return hipErrorInvalidValue;
     const int64_t blocks = static_cast<int64_t>(groups) * ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(gemm_wgrad_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), WLds, st, g);
