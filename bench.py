@@ -98,7 +98,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=0, help="default: 10x --steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration)")
     return ap.parse_args()
