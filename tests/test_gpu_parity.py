@@ -50,6 +50,12 @@ SHAPES = {
         n_shared=1, inter_dim=256, score="sigmoid", route_scale=2.5, act="bf16", weight="fp8",
         seed=15, bias_range=0.05),
     "v3_decode_fp8": C.V3_DECODE_FP8,
+    # more than 256 experts: the gate logits take the 512-wide prefill GEMM tiles;
+    # 8 groups of 48 experts, keep 4
+    "wide_gate_E384": LayerShape(
+        name="wide_gate_E384", T=300, dim=256, n_routed=384, n_groups=8, topk_groups=4,
+        top_k=8, n_shared=1, inter_dim=128, score="sigmoid", route_scale=2.5, act="bf16",
+        weight="bf16", seed=16, bias_range=0.05),
 }
 # full-size shapes: gate on every token, outputs on a token sample
 LARGE = {"v2_T4096": (C.V2_BF16, 12), "v3_prefill_T8192": (C.V3_PREFILL_BF16, 8),
