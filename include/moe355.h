@@ -83,7 +83,8 @@ typedef struct moe_config {
                             MOE_FP8_E4M3_B128 (with act BF16) */
   int32_t add_residual;  /* 1: out includes u_t (the total-output equation); 0: out = FFN terms only */
   int32_t act_quant;     /* 0: the expert GEMMs read activations in act dtype (W8A16 with fp8
-                            weights); 1: FP8 W8A8 (KTransformers DeepSeek page, expert formats):
+                            weights); 1: FP8 W8A8 (DeepSeek-R1 analysis page, training-process
+                            hyper-parameters paragraph: FP8 mixed precision, W8A8):
                             x and the SwiGLU output h are quantised to e4m3 with one fp32 scale
                             per row per 128 columns, s = max|a|/448 (1 for a zero block),
                             code = round-to-nearest-even(a/s), right before each expert GEMM.

@@ -8,9 +8,10 @@ What is computed, and where the pages state it
 ----------------------------------------------
   * DeepSeek-V3 notes page (73biji.xyz/llm_pp_dsv3), "DeepSeek-V3 (model.py
     config)" table: the released layer runs its experts in fp8.
-  * KTransformers DeepSeek page (ktransformers.net), supported formats: FP8
-    W8A8 is one of the expert formats it serves, i.e. both the expert weights
-    and the activations entering the expert GEMMs are 8-bit floats.
+  * DeepSeek-R1 analysis page (deepseek.csdn.net), training-process
+    hyper-parameters paragraph: training uses FP8 mixed precision (W8A8), i.e.
+    both the weights and the activations entering the matrix products are
+    8-bit floats.
   * Everything else (gate, SwiGLU experts, shared expert, combine) is the layer
     of moe_oracle.py, unchanged.
 

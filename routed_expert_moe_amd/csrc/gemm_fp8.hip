@@ -1,5 +1,6 @@
-// Grouped GEMM for FP8 W8A8 experts (KTransformers DeepSeek page, expert
-// formats: FP8 W8A8; DeepSeek-V3 notes page, V3 config table: fp8 experts):
+// Grouped GEMM for FP8 W8A8 experts (DeepSeek-R1 analysis page, training-process
+// hyper-parameters paragraph: FP8 mixed precision, W8A8; DeepSeek-V3 notes page,
+// V3 config table: fp8 experts):
 //     C[rows, n] = sum over 128-wide K blocks b of  sa[row][b] * sw[n/128][b] * (A_q B_q^T)_b
 // with A_q, B_q e4m3 codes, sa the 1 x 128 activation scales and sw the
 // 128 x 128 weight block scales, fp32 accumulation.

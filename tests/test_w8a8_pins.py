@@ -2,8 +2,12 @@
 quantiser and the layer with both expert GEMMs in fp8.
 
 Against: the format's decoder on every code, rounding ties and saturation by
-hand, torch's e4m3 cast, a hand-worked quantisation (tests/golden), the
-quantiser's error bound, and the identical-experts closed form of the layer.
+hand, torch's e4m3 cast, a hand-worked quantisation and a hand-worked W8A8
+SwiGLU FFN (tests/golden), the quantiser's error bound, the per-token
+independence of 1x128 blocks, and the identical-experts closed form of the
+layer.  Planted slips in the FFN (x or h left unquantised, a and c quantised
+in place of h, blocks taken along tokens instead of along a row) each fail at
+least one of these pins.
 """
 import os
 
@@ -122,3 +126,118 @@ def test_h_is_quantised_before_the_down_projection():
     with_hq = w8a8.dequant_1x128(*w8a8.quant_1x128(h)) @ w2.T
     assert np.allclose(got, with_hq, rtol=1e-12, atol=1e-12)
     assert not np.allclose(got, no_hq, rtol=1e-6, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# The W8A8 SwiGLU FFN, pinned by a hand-worked example and by row independence
+# ---------------------------------------------------------------------------
+def _golden_ffn_inputs():
+    """x [1, 128], W13 [256, 128], W2 [128, 128] as the worked example states them."""
+    D = I = 128
+    x = np.zeros((1, D))
+    x[0, :2] = [3.5, 0.3]
+    w13 = np.zeros((2 * I, D))
+    w13[0, 0] = 1.0                       # W1[0] = e0
+    w13[1, 1] = 1.0                       # W1[1] = e1
+    w13[2, 0], w13[2, 1] = 0.5, 1.0       # W1[2] = 0.5 e0 + e1
+    w13[I + 0, 1] = 1.0                   # W3[0] = e1
+    w13[I + 1, 0] = 1.0                   # W3[1] = e0
+    w13[I + 2, 0], w13[I + 2, 1] = 1.0, -2.0   # W3[2] = e0 - 2 e1
+    w2 = np.zeros((D, I))
+    w2[0, 0] = w2[1, 1] = w2[2, 2] = 1.0
+    w2[3, :3] = [0.5, -1.0, 0.25]
+    return x, w13, w2
+
+
+def pin_golden_ffn(ffn) -> bool:
+    g = _fixture("w8a8_ffn_worked_example.txt")
+    x, w13, w2 = _golden_ffn_inputs()
+    out = ffn(x, w13, w2)
+    s_h = float(g["h_scale"])
+    want = np.zeros(128)
+    want[:4] = [float(v) * s_h for v in g["out_over_h_scale"].split()]
+    return bool(np.allclose(out[0], want, rtol=1e-12, atol=1e-15))
+
+
+def pin_rows_independent(ffn) -> bool:
+    """1x128 blocks lie inside one token's row: a token's output cannot depend on the others."""
+    rng = np.random.default_rng(8)
+    T, D, I = 130, 256, 128
+    x = rng.standard_normal((T, D)) * np.exp2(rng.integers(-8, 5, (T, 1)))
+    w13 = rng.standard_normal((2 * I, D)) / 16
+    w2 = rng.standard_normal((D, I)) / 11
+    batch = ffn(x, w13, w2)
+    alone = np.concatenate([ffn(x[t:t + 1], w13, w2) for t in (0, 1, 77, T - 1)])
+    return bool(np.allclose(batch[[0, 1, 77, T - 1]], alone, rtol=1e-12, atol=0))
+
+
+PINS = [pin_golden_ffn, pin_rows_independent]
+
+
+def test_golden_w8a8_ffn_codes():
+    """The quantiser's decisions of the worked example: x and h codes and scales."""
+    g = _fixture("w8a8_ffn_worked_example.txt")
+    x, w13, w2 = _golden_ffn_inputs()
+    xc, xs = w8a8.quant_1x128(x)
+    assert xs[0, 0] == float(g["x_scale"])
+    assert [int(c) for c in xc[0, :2]] == [int(v, 16) for v in g["x_codes"].split()]
+    xq = w8a8.dequant_1x128(xc, xs)
+    h = oracle.silu(xq @ w13[:128].T) * (xq @ w13[128:].T)
+    hc, hs = w8a8.quant_1x128(h)
+    assert hs[0, 0] == np.float32(float(g["h_scale"]))
+    assert [int(c) for c in hc[0, :3]] == [int(v, 16) for v in g["h_codes"].split()]
+    assert not hc[0, 3:].any()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_w8a8_ffn_meets_pin(pin):
+    assert pin(w8a8.swiglu_ffn_w8a8)
+
+
+def _quant_cols(a):
+    """Blocks of 128 consecutive TOKENS of one column (a planted slip), zero-padded."""
+    a = np.asarray(a, np.float64)
+    T = a.shape[0]
+    pad = (-T) % 128
+    at = np.concatenate([a, np.zeros((pad, a.shape[1]))]).T
+    return w8a8.dequant_1x128(*w8a8.quant_1x128(at)).T[:T]
+
+
+def _q(a):
+    return w8a8.dequant_1x128(*w8a8.quant_1x128(a))
+
+
+def _slip_skip_x(x, w13, w2):
+    H = w2.shape[1]
+    return _q(oracle.silu(x @ w13[:H].T) * (x @ w13[H:].T)) @ w2.T
+
+
+def _slip_skip_h(x, w13, w2):
+    H = w2.shape[1]
+    xa = _q(x)
+    return (oracle.silu(xa @ w13[:H].T) * (xa @ w13[H:].T)) @ w2.T
+
+
+def _slip_quant_a_c(x, w13, w2):
+    H = w2.shape[1]
+    xa = _q(x)
+    return (oracle.silu(_q(xa @ w13[:H].T)) * _q(xa @ w13[H:].T)) @ w2.T
+
+
+def _slip_h_transposed(x, w13, w2):
+    H = w2.shape[1]
+    xa = _q(x)
+    return _quant_cols(oracle.silu(xa @ w13[:H].T) * (xa @ w13[H:].T)) @ w2.T
+
+
+def _slip_x_transposed(x, w13, w2):
+    H = w2.shape[1]
+    xa = _quant_cols(x)
+    return _q(oracle.silu(xa @ w13[:H].T) * (xa @ w13[H:].T)) @ w2.T
+
+
+@pytest.mark.parametrize("slip", [_slip_skip_x, _slip_skip_h, _slip_quant_a_c, _slip_h_transposed,
+                                  _slip_x_transposed], ids=lambda f: f.__name__)
+def test_planted_slip_fails_a_pin(slip):
+    failed = [p.__name__ for p in PINS if not p(slip)]
+    assert failed, f"{slip.__name__} passes every pin"
