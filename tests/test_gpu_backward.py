@@ -140,10 +140,16 @@ def test_backward_rejects_unsupported_and_small_workspace():
 
 
 def test_backward_v3_prefill_sampled():
-    """The V3 prefill layer at its full size (T=8192, the batch bench.py times):
-    dx on a seeded sample of tokens and dW13 / dW2 of one expert, against the
-    oracle computed for just those outputs (each depends only on the sampled
-    token's own pairs, or on the rows the expert received)."""
+    """The V3 prefill layer at its full size (T=8192, the batch bench.py times), against
+    the oracle computed for just the sampled outputs, each of which depends on a known
+    part of the batch only:
+      * dx of a token sample (a token's dx involves its own gate row, experts and dout);
+      * dW13 / dW2 of the least and the most loaded expert (the rows it received);
+      * rows e of dW_gate for those experts (with sigmoid scores a token's gate gradient
+        is zero outside its chosen experts, so row e sums over the tokens that chose e);
+      * a seeded slice of 64 hidden units of the shared expert's dW13 (their W1 and W3
+        rows) and dW2 (their columns): SwiGLU hidden units do not interact, so the
+        gradient of the sliced FFN is the slice of the full gradient."""
     import oracle
     from routed_expert_moe_amd import configs
     s = configs.V3_PREFILL_BF16
@@ -157,28 +163,46 @@ def test_backward_v3_prefill_sampled():
     x64 = to_f64(layer.x)
     wg64 = to_f64(layer.w_gate)
     d64 = to_f64(dout)
-    get = expert_fn(layer)
+    get = expert_fn(layer, fast=True)
     sh = shared_pair(layer)
 
     # dx of sampled tokens: the oracle's backward restricted to those tokens is
     # exact, since dx_t only involves token t's gate row, experts and dout_t
     rng = np.random.default_rng(2024)
-    toks = np.sort(rng.choice(s.T, 12, replace=False))
+    toks = np.sort(rng.choice(s.T, 48, replace=False))
+    toks[-1] = s.T - 1
     want = obw.moe_layer_backward(x64[toks], wg64, bias_f64(layer), get, sh, spec, d64[toks],
                                   force_idx=idx[toks]).dx
     err = rel_err(to_f64(g.dx)[toks], want)
-    say(f"  dx (12 tokens) {err:.3g}")
+    say(f"  dx ({toks.size} tokens) {err:.3g}")
     assert err <= TOL
 
-    # one expert's weight gradients from every row it received
     counts = np.bincount(idx.ravel(), minlength=s.n_routed)
-    e = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
-    rows, slot = np.nonzero(idx == e)
+    least = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    busiest = int(np.argmax(counts))
     gt = oracle.gate(x64, wg64, bias_f64(layer), spec, force_idx=idx)
-    w13, w2 = get(e)
-    dy = gt.w[rows, slot][:, None] * d64[rows]
-    _, dw13, dw2 = obw.swiglu_ffn_backward(x64[rows], w13, w2, dy)
-    e13 = rel_err(g.dw13[e].cpu().numpy(), dw13)
-    e2 = rel_err(g.dw2[e].cpu().numpy(), dw2)
-    say(f"  expert {e} ({rows.size} rows): dw13 {e13:.3g} dw2 {e2:.3g}")
+    dwg = g.dw_gate.cpu().numpy()
+    for e in (least, busiest):
+        # the expert's weight gradients from every row it received
+        rows, slot = np.nonzero(idx == e)
+        w13, w2 = get(e)
+        dy = gt.w[rows, slot][:, None] * d64[rows]
+        _, dw13, dw2 = obw.swiglu_ffn_backward(x64[rows], w13, w2, dy)
+        e13 = rel_err(g.dw13[e].cpu().numpy(), dw13)
+        e2 = rel_err(g.dw2[e].cpu().numpy(), dw2)
+        # row e of dW_gate: the backward of the tokens that chose e
+        ref = obw.moe_layer_backward(x64[rows], wg64, bias_f64(layer), get, sh, spec, d64[rows],
+                                     force_idx=idx[rows])
+        eg = rel_err(dwg[e], ref.dw_gate[e])
+        say(f"  expert {e} ({rows.size} rows): dw13 {e13:.3g} dw2 {e2:.3g} dw_gate[e] {eg:.3g}")
+        assert e13 <= TOL and e2 <= TOL and eg <= TOL
+
+    # the shared expert on a slice of its hidden units, over all tokens (dz = dout)
+    SI = s.n_shared * s.inter_dim
+    J = np.sort(rng.choice(SI, 64, replace=False))
+    sw13, sw2 = sh
+    _, d13, d2 = obw.swiglu_ffn_backward(x64, sw13[np.concatenate([J, SI + J])], sw2[:, J], d64)
+    e13 = rel_err(g.dsw13.cpu().numpy()[np.concatenate([J, SI + J])], d13)
+    e2 = rel_err(g.dsw2.cpu().numpy()[:, J], d2)
+    say(f"  shared expert, 64 hidden units: dsw13 {e13:.3g} dsw2 {e2:.3g}")
     assert e13 <= TOL and e2 <= TOL

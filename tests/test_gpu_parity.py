@@ -58,8 +58,8 @@ SHAPES = {
         weight="bf16", seed=16, bias_range=0.05),
 }
 # full-size shapes: gate on every token, outputs on a token sample
-LARGE = {"v2_T4096": (C.V2_BF16, 12), "v3_prefill_T8192": (C.V3_PREFILL_BF16, 8),
-         "v3_ep_shard_T4096": (C.V3_EP_SHARD_BF16, 12)}
+LARGE = {"v2_T4096": (C.V2_BF16, 256), "v3_prefill_T8192": (C.V3_PREFILL_BF16, 256),
+         "v3_ep_shard_T4096": (C.V3_EP_SHARD_BF16, 128)}
 
 _cache = {}
 
@@ -128,7 +128,7 @@ def check_forward(layer, tokens=None):
     shape = layer.shape
     say(f"[moe_forward] {shape.name} T={layer.x.shape[0]} sample={None if tokens is None else len(tokens)}")
     out, idx, w = run_forward(layer)
-    ref, g = run_oracle(layer, tokens=tokens, force_idx=idx)
+    ref, g = run_oracle(layer, tokens=tokens, force_idx=idx, fast=tokens is not None)
     # the GPU's selection must be certified-equal to the oracle's own (checked in the gate test);
     # here the values are compared on the GPU's selection
     got = to_f64(out)
@@ -313,13 +313,12 @@ def test_imbalanced_routing_many_tiles():
     assert rel_err(to_f64(out), ref) <= TOL["bf16"]
 
 
-def test_expert_rows_full_size_v3():
-    """y_pairs rows and the shared output z at the V3 prefill size, against the oracle FFN."""
-    layer = layer_for(C.V3_PREFILL_BF16)
+def _expert_rows(layer):
+    """gate -> permute -> expert_ffn on the GPU; returns the routing arrays, h, y_pairs, z."""
     shape = layer.shape
     cfg = B.config_of(shape)
     T, K, D, I = shape.T, shape.top_k, shape.dim, shape.inter_dim
-    say("[moe_expert_ffn] v3 full size rows")
+    SI = shape.n_shared * I
     logits = torch.empty(T, shape.n_routed, dtype=torch.float32, device="cuda")
     idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
     w = torch.empty(T, K, dtype=torch.float32, device="cuda")
@@ -328,23 +327,52 @@ def test_expert_rows_full_size_v3():
     B.moe_permute(cfg, T, idx, r)
     h = torch.empty(r.struct.max_rows, I, dtype=torch.bfloat16, device="cuda")
     y = torch.empty(r.struct.max_rows, D, dtype=torch.bfloat16, device="cuda")
-    hs = torch.empty(T, I, dtype=torch.bfloat16, device="cuda")
-    z = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
+    hs = torch.empty(T, SI, dtype=torch.bfloat16, device="cuda") if SI else None
+    z = torch.empty(T, D, dtype=torch.bfloat16, device="cuda") if SI else None
     B.moe_expert_ffn(cfg, T, layer.x, r, B.weights_of(layer), h, y, hs, z)
     torch.cuda.synchronize()
-    counts = r.counts.cpu().numpy()
-    off = r.expert_off.cpu().numpy()
-    sp = r.sorted_pair.cpu().numpy()
-    # the busiest expert (several tiles) and two others, first/last rows of each
+    return (r.counts.cpu().numpy(), r.expert_off.cpu().numpy(), r.sorted_pair.cpu().numpy(), h, y, z)
+
+
+def _spread_experts(counts: np.ndarray, n: int = 16):
+    """The busiest and the least loaded expert, plus n experts spread evenly over the index range
+    (so their rows sit in every part of the expert-sorted work list)."""
     used = np.nonzero(counts > 0)[0]
-    experts = [int(np.argmax(counts)), int(used[np.argmin(counts[used])]), int(used[len(used) // 2])]
-    get = expert_fn(layer)
+    pick = {int(np.argmax(counts)), int(used[np.argmin(counts[used])])}
+    pick.update(int(used[i]) for i in np.linspace(0, used.size - 1, n).round().astype(int))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("shape", [C.V3_PREFILL_BF16, C.V2_BF16], ids=lambda s: s.name)
+def test_expert_rows_full_size(shape):
+    """Every h and y_pairs row of 18 experts at full size against the oracle's SwiGLU,
+    and the shared output z on a token sample."""
+    layer = layer_for(shape)
+    K = shape.top_k
+    say(f"[moe_expert_ffn] {shape.name} full size rows")
+    counts, off, sp, h, y, z = _expert_rows(layer)
+    get = expert_fn(layer, fast=True)
     x64 = to_f64(layer.x)
+    experts = _spread_experts(counts)
+    worst_h = worst_y = 0.0
+    nrows = 0
     for e in experts:
-        rows = [off[e], off[e] + counts[e] - 1, off[e] + counts[e] // 2]
+        rows = np.arange(off[e], off[e] + counts[e])
         toks = sp[rows] // K
-        ref = oracle.swiglu_ffn(x64[toks], *get(e))
-        assert rel_err(to_f64(y[rows]), ref) <= TOL["bf16"], e
-    toks = np.array([0, 1, T // 2, T - 1])
-    ref = oracle.swiglu_ffn(x64[toks], *shared_pair(layer))
-    assert rel_err(to_f64(z[toks]), ref) <= TOL["bf16"]
+        w13, w2 = get(e)
+        I = w13.shape[0] // 2
+        hr = oracle.silu(x64[toks] @ w13[:I].T) * (x64[toks] @ w13[I:].T)
+        rt = torch.as_tensor(rows, device="cuda")
+        eh = rel_err(to_f64(h[rt]), hr)
+        ey = rel_err(to_f64(y[rt]), hr @ w2.T)
+        worst_h, worst_y = max(worst_h, eh), max(worst_y, ey)
+        nrows += rows.size
+        assert eh <= TOL["bf16"] and ey <= TOL["bf16"], (e, eh, ey)
+    say(f"  {len(experts)} experts, {nrows} rows: worst h {worst_h:.3g}, y_pairs {worst_y:.3g}")
+    if z is not None:
+        rng = np.random.default_rng(shape.seed + 7)
+        toks = np.sort(rng.choice(shape.T, 128, replace=False))
+        ref = oracle.swiglu_ffn(x64[toks], *shared_pair(layer))
+        ez = rel_err(to_f64(z[torch.as_tensor(toks, device="cuda")]), ref)
+        say(f"  shared z (128 tokens) {ez:.3g}")
+        assert ez <= TOL["bf16"]

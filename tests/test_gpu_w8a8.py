@@ -2,17 +2,32 @@
 1 x 128 to e4m3 before each expert GEMM) against the W8A8 oracle.
 
 The quantisation of x is compared code for code and scale for scale (both
-sides decide in float32 from the exact bf16 inputs).  The layer output is
-compared on the GPU's expert selection within the fp8 tolerance, on h' and on
-h' - u; the SwiGLU output h is quantised from each side's own fp32 value, so a
-code may differ where the two straddle a rounding midpoint.
+sides decide in float32 from the exact bf16 inputs).  The SwiGLU output h is
+quantised from each side's own fp32 value.  The fp8 MFMA
+(v_mfma_scale_f32_32x32x64_f8f6f4) sums the 64 products of one instruction to
+about 14 bits relative to the largest product (measured on the GPU with one
+instruction on fixed operands: 30 products of 0.125 next to two of 448^2 that
+cancel come out 1.5 short; random operands land within 2^-14 of the largest
+product), so the GPU's gate/up values differ from the exact ones by up to about
+1e-4 of a block's largest h.  The GPU's h codes and scales (read back from the
+h buffer) are therefore compared with the oracle's quantisation of its own h on
+the same rows by what that allows: scales within 2^-12 relative, every decoded
+value within half an e4m3 step of each side's own value plus 2^-12 of the
+block maximum, and at least 99.5% of codes equal (a code moves only where h
+sits that close to a rounding midpoint).  The layer output is compared on the
+GPU's expert selection within the bf16 tolerance 2e-2: once the quantisers'
+decisions agree, the two sides differ by the bf16 roundings of y_pairs and the
+output, as in the bf16 layer; the fp8 tolerance 6e-2 would not see a misplaced
+h quantisation.  Activation blocks that are all zero (scale 1) or tiny (amax
+1e-30) are fed on purpose.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import w8a8
-from oracle_bridge import run_oracle, to_f64
+from oracle_bridge import expert_fn, run_oracle, shared_pair, to_f64
 from parity import TOL, rel_err, say
 from routed_expert_moe_amd import binding as B
 from routed_expert_moe_amd import configs, synth
@@ -76,14 +91,15 @@ def _check(layer, tokens=None):
     w = torch.empty(T, K, dtype=torch.float32, device="cuda")
     out = mod.forward(layer.x, topk_idx=idx, topk_w=w)
     torch.cuda.synchronize()
-    ref, _ = run_oracle(layer, tokens=tokens, force_idx=idx.cpu().numpy().astype(np.int64))
+    ref, _ = run_oracle(layer, tokens=tokens, force_idx=idx.cpu().numpy().astype(np.int64),
+                        fast=tokens is not None)
     got, u = to_f64(out), to_f64(layer.x)
     if tokens is not None:
         got, u = got[tokens], u[tokens]
     e_out, e_ffn = rel_err(got, ref), rel_err(got - u, ref - u)
-    say(f"  rel err h'={e_out:.3g}  h'-u={e_ffn:.3g}  tol={TOL['fp8']}")
+    say(f"  rel err h'={e_out:.3g}  h'-u={e_ffn:.3g}  tol={TOL['bf16']}")
     assert np.all(np.isfinite(got))
-    assert e_out <= TOL["fp8"] and e_ffn <= TOL["fp8"]
+    assert e_out <= TOL["bf16"] and e_ffn <= TOL["bf16"]
     return out, idx, w
 
 
@@ -95,9 +111,49 @@ def test_w8a8_forward_parity(name):
 def test_w8a8_v3_prefill_sampled():
     shape = configs.V3_PREFILL_W8A8
     rng = np.random.default_rng(shape.seed + 100)
-    toks = np.sort(rng.choice(shape.T, size=8, replace=False))
+    toks = np.sort(rng.choice(shape.T, size=256, replace=False))
     toks[-1] = shape.T - 1
     _check(_layer(shape), tokens=toks)
+
+
+def test_w8a8_expert_rows_v3_prefill():
+    """Every y_pairs row of 18 experts at the V3 prefill size (the busiest, the least loaded
+    and 16 spread over the expert range) against the oracle's W8A8 SwiGLU of those rows."""
+    layer = _layer(configs.V3_PREFILL_W8A8)
+    shape = layer.shape
+    cfg = B.config_of(shape)
+    T, E, K, D, I = shape.T, shape.n_routed, shape.top_k, shape.dim, shape.inter_dim
+    say(f"[moe_expert_ffn w8a8] {shape.name} full size rows")
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    B.moe_gate(cfg, T, layer.x, layer.w_gate, layer.bias, logits, idx, w)
+    r = B.make_routing(cfg, T)
+    B.moe_permute(cfg, T, idx, r)
+    B.moe_quant_act(cfg, T, layer.x, r)
+    h = torch.empty(r.struct.max_rows, I, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(r.struct.max_rows, D, dtype=torch.bfloat16, device="cuda")
+    hs = torch.empty(T, shape.n_shared * I, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
+    B.moe_expert_ffn(cfg, T, layer.x, r, B.weights_of(layer), h, y, hs, z)
+    torch.cuda.synchronize()
+    counts = r.counts.cpu().numpy()
+    off = r.expert_off.cpu().numpy()
+    sp = r.sorted_pair.cpu().numpy()
+    used = np.nonzero(counts > 0)[0]
+    experts = {int(np.argmax(counts)), int(used[np.argmin(counts[used])])}
+    experts.update(int(used[i]) for i in np.linspace(0, used.size - 1, 16).round().astype(int))
+    get = expert_fn(layer, fast=True)
+    x64 = to_f64(layer.x)
+    worst = 0.0
+    for e in sorted(experts):
+        rows = np.arange(off[e], off[e] + counts[e])
+        w13, w2 = get(e)
+        ref = w8a8.swiglu_ffn_w8a8(x64[sp[rows] // K], w13, w2)
+        err = rel_err(to_f64(y[torch.as_tensor(rows, device="cuda")]), ref)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (e, err)
+    say(f"  {len(experts)} experts: worst y_pairs {worst:.3g}")
 
 
 def test_w8a8_steps_equal_forward():
@@ -127,3 +183,150 @@ def test_w8a8_steps_equal_forward():
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(w, w2)
     assert torch.equal(out, out2)
+
+
+def _e4m3_step(codes: np.ndarray) -> np.ndarray:
+    """Spacing of e4m3 values around each code (in code units; times the scale gives the value)."""
+    e = (codes.astype(np.int64) >> 3) & 0xF
+    return np.where(e == 0, 2.0 ** -9, np.exp2(e.astype(np.float64) - 7.0 - 3.0))
+
+
+def _h_readback(h: torch.Tensor, rows: int, cols: int):
+    """The W8A8 h buffer: rows*cols e4m3 codes, then (at the next 256-byte boundary) fp32 scales."""
+    raw = h.view(torch.uint8).reshape(-1)
+    codes = raw[: rows * cols].reshape(rows, cols)
+    off = (rows * cols + 255) // 256 * 256
+    scales = raw[off: off + 4 * rows * (cols // 128)].view(torch.float32).reshape(rows, cols // 128)
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+H_REL = 2.0 ** -12   # bound on |h_gpu - h_oracle| relative to the block maximum (fp8 MFMA sums)
+
+
+def _compare_h(name, got_c, got_s, ref_c, ref_s):
+    eq = got_c == ref_c
+    frac = float(eq.mean())
+    gs = np.repeat(got_s.astype(np.float64), 128, axis=1)
+    rs = np.repeat(ref_s.astype(np.float64), 128, axis=1)
+    vg = oracle.decode_e4m3(got_c) * gs
+    vr = oracle.decode_e4m3(ref_c) * rs
+    amax = rs * 448.0
+    slack = 0.5 * _e4m3_step(got_c) * gs + 0.5 * _e4m3_step(ref_c) * rs + H_REL * amax
+    excess = float(np.max((np.abs(vg - vr) - slack) / np.maximum(amax, 1e-300)))
+    srel = np.abs(got_s.astype(np.float64) - ref_s) / np.maximum(np.abs(ref_s.astype(np.float64)), 1e-300)
+    say(f"  {name}: {got_c.size} codes, equal {frac:.6f}, max scale rel diff {float(srel.max()):.3g}, "
+        f"max value excess over the bound {excess:.3g} of the block max")
+    assert frac >= 0.995
+    assert srel.max() <= H_REL
+    assert excess <= 0.0
+
+
+def _up_readback(layer):
+    """gate -> permute -> quant_act -> expert_up; returns the routing, h and hs read back."""
+    shape = layer.shape
+    cfg = B.config_of(shape)
+    x = layer.x
+    T, E, K, I = shape.T, shape.n_routed, shape.top_k, shape.inter_dim
+    SI = shape.n_shared * I
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    B.moe_gate(cfg, T, x, layer.w_gate, layer.bias, logits, idx, w)
+    r = B.make_routing(cfg, T)
+    B.moe_permute(cfg, T, idx, r)
+    B.moe_quant_act(cfg, T, x, r)
+    h = torch.empty(r.struct.max_rows, I, dtype=torch.bfloat16, device="cuda")
+    hs = torch.empty(T, max(SI, 1), dtype=torch.bfloat16, device="cuda") if SI else None
+    B.moe_expert_up(cfg, T, x, r, B.weights_of(layer), h, hs)
+    torch.cuda.synchronize()
+    hc, hsc = _h_readback(h, r.struct.max_rows, I)
+    sc = ss = None
+    if SI:
+        sc, ss = _h_readback(hs, T, SI)
+    return r, hc, hsc, sc, ss
+
+
+def _oracle_h(xq: np.ndarray, w13: np.ndarray) -> np.ndarray:
+    H = w13.shape[0] // 2
+    return oracle.silu(xq @ w13[:H].T) * (xq @ w13[H:].T)
+
+
+def _check_h_codes(layer, experts=None):
+    shape = layer.shape
+    say(f"[moe_expert_up w8a8 h codes] {shape.name}")
+    r, hc, hsc, sc, ss = _up_readback(layer)
+    K = shape.top_k
+    xq = w8a8.dequant_1x128(*w8a8.quant_1x128(to_f64(layer.x).astype(np.float32)))
+    counts = r.counts.cpu().numpy()
+    off = r.expert_off.cpu().numpy()
+    sp = r.sorted_pair.cpu().numpy()
+    get = expert_fn(layer)
+    used = np.nonzero(counts > 0)[0] if experts is None else np.asarray(experts)
+    gc, gs, rc, rs = [], [], [], []
+    for e in used:
+        rows = np.arange(off[e], off[e] + counts[e])
+        toks = sp[rows] // K
+        w13, _ = get(int(e))
+        c, s = w8a8.quant_1x128(_oracle_h(xq[toks], w13))
+        gc.append(hc[rows]); gs.append(hsc[rows]); rc.append(c); rs.append(s)
+    _compare_h("routed h", np.concatenate(gc), np.concatenate(gs), np.concatenate(rc), np.concatenate(rs))
+    if sc is not None:
+        c, s = w8a8.quant_1x128(_oracle_h(xq, shared_pair(layer)[0]))
+        _compare_h("shared hs", sc, ss, c, s)
+
+
+@pytest.mark.parametrize("name", ["w8a8_small", "w8a8_ragged_2shared", "w8a8_softmax_noshared"])
+def test_w8a8_h_codes_match_oracle(name):
+    _check_h_codes(_layer(SHAPES[name]))
+
+
+def test_w8a8_h_codes_v3_prefill_experts():
+    """At the V3 prefill size: every h row of the busiest, the least loaded and a middle expert."""
+    layer = _layer(configs.V3_PREFILL_W8A8)
+    # the expert loads come from one routing pass
+    r, _, _, _, _ = _up_readback(layer)
+    counts = r.counts.cpu().numpy()
+    used = np.nonzero(counts > 0)[0]
+    order = used[np.argsort(counts[used], kind="stable")]
+    experts = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2])})
+    del r
+    _check_h_codes(layer, experts=experts)
+
+
+BLOCKS = LayerShape(
+    name="w8a8_zero_tiny_blocks", T=256, dim=512, n_routed=16, n_groups=4, topk_groups=2, top_k=4,
+    n_shared=1, inter_dim=256, score="sigmoid", route_scale=2.5, act="bf16", weight="fp8",
+    act_quant=1, seed=45, bias_range=0.05)
+
+
+def _blocky_layer():
+    """x with all-zero and tiny-amax (1e-30) 128-column blocks in many rows, in every position."""
+    layer = _layer(BLOCKS)
+    x = layer.x.float().cpu()
+    T, D = x.shape
+    for t in range(T):
+        kind = t % 6
+        b = (t // 6) % (D // 128)
+        blk = slice(128 * b, 128 * (b + 1))
+        if kind == 1:
+            x[t, blk] = 0.0
+        elif kind == 2:
+            x[t, blk] *= 1e-30 / x[t, blk].abs().max()
+        elif kind == 3:                      # a tiny block right after a zero block
+            x[t, blk] = 0.0
+            nb = slice(128 * ((b + 1) % (D // 128)), 128 * ((b + 1) % (D // 128) + 1))
+            x[t, nb] *= 1e-30 / x[t, nb].abs().max()
+        elif kind == 4 and t % 12 == 4:      # a whole row of tiny blocks
+            x[t] *= 1e-30 / x[t].abs().max()
+    x[T - 1] = 0.0                           # one all-zero token
+    layer.x = x.to(torch.bfloat16).cuda()
+    return layer
+
+
+def test_w8a8_zero_and_tiny_activation_blocks():
+    layer = _blocky_layer()
+    xb = to_f64(layer.x).astype(np.float32).reshape(layer.shape.T, -1, 128)
+    amax = np.abs(xb).max(axis=2)
+    assert (amax == 0).sum() > 20 and ((amax > 0) & (amax <= 1e-30)).sum() > 20
+    _check_h_codes(layer)
+    _check(layer)
