@@ -1,23 +1,33 @@
 """Benchmark: forward pass of one DeepSeekMoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
 
 A step is one pass of the whole layer (gate, dispatch, routed expert FFNs,
 shared expert, combine) over one batch of synthetic tokens already resident
 in HBM.  The headline workload is the V3-shaped prefill layer (T=8192, dim
 7168, 256 routed experts in 8 groups keep 4, top-8, 1 shared, inter 2048,
-bf16); the 8-token fp8 decode step of the same layer is reported beside it.
-Prints one JSON line.  Random-init weights of the layer's architecture and
-x ~ N(0,1), as described in synth.py.
+bf16).  Beside it the same JSON line reports the other layer shapes: the
+8-token fp8 decode step of the V3 layer, the V3 prefill batch in FP8 W8A8, a
+V2-Lite-shaped chunk (T=512), a V2-shaped layer (T=4096), the tiny fp32 layer
+(T=64) and one GPU's expert-parallel share of the V3 layer.  Random-init
+weights of the layer's architecture and x ~ N(0,1), as described in synth.py.
+
+Timing: HIP events on the launch stream around every step and every stage of
+it (gate, dispatch, gate/up GEMM, down GEMM, combine); mean, median, min and
+p90 over the timed steps.  `ms_per_step` is the whole timed region divided by
+the number of steps.
 
 roofline: the dominant kernel is the gate/up grouped GEMM (moe_expert_up);
-its duration comes from HIP events recorded around it on the stream it runs
-on, inside the timed region.  Its algorithmic work per launch is
-2*T*K*(2I)*D + 2*T*(2*S*I)*D flops and the bytes of the touched experts'
-W1/W3 (plus block scales), the shared W1/W3, x and the written h.  The bound
-reported is the ceiling that binds: with all 256 experts touched the prefill
-kernel's bytes take longer at 8 TB/s than its flops at 2.5 PFLOP/s, so it is
-HBM-bound on the roofline; both fractions are reported.
+its average duration over the timed steps comes from those events.  Its
+algorithmic work per launch is 2*T*K*(2I)*D + 2*T*(2*S*I)*D flops and the
+bytes of the touched experts' W1/W3 (plus block scales), the shared W1/W3,
+x and the written h.  The bound reported is the ceiling that binds (the flops
+at the dtype's MFMA peak against the bytes at 8 TB/s); both fractions are
+reported.
+
+cpu_baseline: the float64 oracle on a token sample of the headline workload,
+on the host's cores; the expert weights are decoded to float64 outside the
+timed region, so only the oracle's own arithmetic is timed.
 """
 from __future__ import annotations
 
@@ -30,6 +40,7 @@ import time
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector)
 
 # Measured HBM traffic per launch of the roofline kernels: rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the layer's
@@ -98,10 +109,17 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=0, help="default: 10x --steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens of the headline workload the CPU oracle is timed on")
+    ap.add_argument("--only", default="",
+                    help="comma-separated workloads to time (default: all); names as in the JSON")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+STAGES = ("gate", "dispatch", "up", "down", "combine")
 
 
 class Pass:
@@ -130,19 +148,23 @@ class Pass:
         self.z = torch.empty(T, D, dtype=act, device=dev) if S else None
         self.out = torch.empty(T, D, dtype=act, device=dev)
 
-    def step(self, ev_up=None):
+    def step(self, ev=None):
+        """One layer pass; ev = 6 events recorded at the stage boundaries (or None)."""
         B, L = self.B, self.layer
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
         B.moe_gate(self.cfg, self.T, L.x, L.w_gate, L.bias, self.logits, self.idx, self.tw)
+        rec(1)
         B.moe_permute(self.cfg, self.T, self.idx, self.r)
         if self.cfg.act_quant:
             B.moe_quant_act(self.cfg, self.T, L.x, self.r)
-        if ev_up is not None:
-            ev_up[0].record()
+        rec(2)
         B.moe_expert_up(self.cfg, self.T, L.x, self.r, self.w, self.h, self.hs)
-        if ev_up is not None:
-            ev_up[1].record()
+        rec(3)
         B.moe_expert_down(self.cfg, self.T, self.r, self.w, self.h, self.hs, self.y, self.z)
+        rec(4)
         B.moe_combine(self.cfg, self.T, L.x, self.z, self.y, self.r, self.tw, self.out)
+        rec(5)
 
 
 def work_figures(layer, counts):
@@ -172,12 +194,23 @@ def progress(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_pass(p: Pass, steps: int, warmup: int):
+def stats(v) -> dict:
+    import numpy as np
+    a = np.asarray(v, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "min": float(a.min()),
+            "p90": float(np.percentile(a, 90))}
+
+
+def time_pass(p: Pass, steps: int, warmup: int) -> dict:
+    """Times `steps` layer passes after `warmup` untimed ones.
+
+    Returns the whole region's milliseconds, the host wall time, and per-stage and
+    per-step times from events recorded between the launches on the launch stream."""
     import torch
     for _ in range(warmup):
         p.step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -188,9 +221,63 @@ def time_pass(p: Pass, steps: int, warmup: int):
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
-    up_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-    return total_ms, up_ms, wall
+    per = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(STAGES)}
+    per["step"] = [e[0].elapsed_time(e[5]) for e in evs]
+    return {"total_ms": t0.elapsed_time(t1), "wall_s": wall, "per": per}
+
+
+def layer_report(p: Pass, t: dict, steps: int, peak_tflops: float, traffic_key=None,
+                 kernel: str = "moe_expert_up (gate/up grouped GEMM + SwiGLU)") -> dict:
+    """The per-workload record: throughput, step statistics, stage medians, roofline."""
+    layer, s = p.layer, p.layer.shape
+    fig = work_figures(layer, p.r.counts.cpu().numpy())
+    ms = t["total_ms"] / steps
+    up_ms = stats(t["per"]["up"])["mean"]
+    return {
+        "workload": s.name, "T": s.T, "dim": s.dim, "n_routed": s.n_routed, "top_k": s.top_k,
+        "n_shared": s.n_shared, "inter_dim": s.inter_dim, "score": s.score,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights (128x128 fp32 scales)"}[s.weight]
+                 + (" x fp8-e4m3 activations (1x128 fp32 scales)" if s.act_quant else ""),
+        "steps": steps, "ms_per_step": ms, "tokens_per_s": s.T / (ms / 1e3),
+        "step_ms": stats(t["per"]["step"]),
+        "stage_ms_median": {k: stats(t["per"][k])["median"] for k in STAGES},
+        "experts_touched": fig["touched"],
+        "layer": {"flops": fig["flops_layer"], "bytes": fig["bytes_layer"],
+                  "tflops": fig["flops_layer"] / (ms / 1e3) / 1e12,
+                  "mfma_frac": fig["flops_layer"] / (ms / 1e3) / 1e12 / peak_tflops,
+                  "gbs": fig["bytes_layer"] / (ms / 1e3) / 1e9,
+                  "hbm_frac": fig["bytes_layer"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                  "floor_ms": max(fig["flops_layer"] / (peak_tflops * 1e9),
+                                  fig["bytes_layer"] / (PEAK_HBM_GBS * 1e6))},
+        "roofline": roofline(fig["flops_up"], fig["bytes_up"], up_ms,
+                             measured_traffic(traffic_key) if traffic_key else None, kernel, peak_tflops),
+    }
+
+
+def run_workload(shape, steps: int, warmup: int, peak_tflops: float, traffic_key=None, kernel=None,
+                 keep=False):
+    import torch
+    from routed_expert_moe_amd import synth
+    progress(f"building {shape.name}")
+    dev = "cpu" if shape.T * shape.dim * shape.n_routed < 2 ** 27 else "cuda"
+    layer = synth.make_layer(shape, device=dev)
+    if dev == "cpu":
+        for f in ("x", "w_gate", "bias", "w13", "w2", "sw13", "sw2", "w13_scale", "w2_scale",
+                  "sw13_scale", "sw2_scale"):
+            if getattr(layer, f) is not None:
+                setattr(layer, f, getattr(layer, f).cuda())
+    progress(f"timing {shape.name} ({steps} steps)")
+    p = Pass(layer)
+    t = time_pass(p, steps, warmup)
+    kw = {} if kernel is None else {"kernel": kernel}
+    rep = layer_report(p, t, steps, peak_tflops, traffic_key, **kw)
+    rep["_wall_s"] = t["wall_s"]
+    rep["_total_ms"] = t["total_ms"]
+    if keep:
+        return rep, p
+    del p, layer
+    torch.cuda.empty_cache()
+    return rep, None
 
 
 def time_bias_update(p: Pass, shape, calls: int = 200):
@@ -261,20 +348,20 @@ def time_backward(p: Pass, shape, calls: int = 3):
         B.moe_backward(p.cfg, T, L.x, p.w, p.r, p.idx, p.tw, p.logits, p.y, dout, grads, workspace=ws)
     one()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(calls):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in evs:
+        a.record()
         one()
-    b.record()
+        b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / calls
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = sum(times) / calls
     P = T * K
     up = 2 * P * 2 * I * D + 2 * T * 2 * S * I * D
     down = 2 * P * D * I + 2 * T * D * S * I
     flops = 3 * up + 2 * down + 4 * T * E * D
     res = {"what": "moe_backward: dx, dW_gate, routed and shared dW13/dW2 for one upstream gradient",
-           "ms_per_call": ms, "tokens_per_s": T / (ms / 1e3), "gemm_flops": flops,
+           "ms_per_call": ms, "call_ms": stats(times), "tokens_per_s": T / (ms / 1e3), "gemm_flops": flops,
            "tflops": flops / (ms / 1e3) / 1e12, "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
            "workspace_bytes": ws.numel()}
     del grads, ws
@@ -282,50 +369,80 @@ def time_backward(p: Pass, shape, calls: int = 3):
     return res
 
 
-def time_ep_shard(args):
-    """One GPU's share of the V3 prefill layer under expert parallelism (32 local
-    experts, the tokens dispatched to them, no shared expert): the same step
-    sequence on that share, without the collectives that would feed it."""
-    import torch
-    from routed_expert_moe_amd import configs, synth
-    shape = configs.V3_EP_SHARD_BF16
-    layer = synth.make_layer(shape, device="cuda")
-    p = Pass(layer)
-    total_ms, up_ms, _ = time_pass(p, args.steps, args.warmup)
-    fig = work_figures(layer, p.r.counts.cpu().numpy())
-    ms = total_ms / args.steps
-    res = {"workload": shape.name, "T": shape.T, "n_routed": shape.n_routed, "top_k": shape.top_k,
-           "what": "one GPU's expert-parallel share of v3_prefill_bf16_T8192 (a local routing of the "
-                   "dispatched tokens stands in for the global gate; no collectives)",
-           "ms_per_step": ms, "pairs": shape.T * shape.top_k, "experts_touched": fig["touched"],
-           "layer_tflops": fig["flops_layer"] / (ms / 1e3) / 1e12,
-           "roofline": roofline(fig["flops_up"], fig["bytes_up"], up_ms, None,
-                                "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")}
-    del p, layer
-    torch.cuda.empty_cache()
-    return res
+def host_info() -> dict:
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cores_available": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(layer, n_tokens: int):
-    """The float64 oracle on the first n_tokens tokens of the same workload, on host cores."""
-    import numpy as np
+def _oracle_time(layer, tokens=None, single_thread=False) -> dict:
+    """Seconds of the float64 oracle's layer forward, weight decoding excluded.
+
+    The oracle takes each expert's weights through a callable; the time spent
+    inside it (copying the stored weights to the host and decoding them to
+    float64) is measured and subtracted, so what remains is the oracle's own
+    arithmetic: gate, the touched experts' SwiGLU FFNs, shared expert, combine."""
     import threadpoolctl
     sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
     import oracle
+    from oracle import w8a8
     from oracle_bridge import bias_f64, expert_fn, shared_pair, spec_of, to_f64
-    x = to_f64(layer.x[:n_tokens])
+    xs = layer.x if tokens is None else layer.x[:tokens]
+    x = to_f64(xs)
     wg = to_f64(layer.w_gate)
     b = bias_f64(layer)
     shared = shared_pair(layer)
-    t0 = time.perf_counter()
-    oracle.moe_layer(x, wg, b, expert_fn(layer), shared, spec_of(layer.shape))
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"first {n_tokens} tokens of the {layer.shape.name} workload, whole layer "
-                       f"(gate, {layer.shape.top_k} routed + shared SwiGLU experts, combine) in "
-                       f"float64; expert weights decoded from device copies inside the timed call; "
-                       f"{dt:.1f} s")}
+    fetch = expert_fn(layer, fast=True)
+    spent = [0.0]
+
+    def expert(e):
+        t = time.perf_counter()
+        w = fetch(e)
+        spent[0] += time.perf_counter() - t
+        return w
+    fn = w8a8.moe_layer_w8a8 if layer.shape.act_quant else oracle.moe_layer
+    limit = threadpoolctl.threadpool_limits(1) if single_thread else None
+    try:
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        fn(x, wg, b, expert, shared, spec_of(layer.shape))
+        dt = time.perf_counter() - t0 - spent[0]
+    finally:
+        if limit is not None:
+            limit.unregister()
+    n = x.shape[0]
+    return {"tokens": n, "seconds": dt, "tokens_per_s": n / dt, "threads": threads,
+            "decode_seconds_excluded": spent[0]}
+
+
+def cpu_baseline(layer, n_tokens: int) -> dict:
+    """The float64 oracle on the first n_tokens tokens of the headline workload, on host cores."""
+    r = _oracle_time(layer, tokens=n_tokens)
+    out = {"value": r["tokens_per_s"], "unit": "tokens/s", "cores": r["threads"], "kind": "oracle",
+           "sample": (f"first {n_tokens} tokens of the {layer.shape.name} workload, whole layer (gate on "
+                      f"those tokens, {layer.shape.top_k} routed + shared SwiGLU experts, combine) in "
+                      f"float64 on {r['threads']} BLAS threads; {r['seconds']:.1f} s of oracle arithmetic "
+                      f"(expert weight decoding, {r['decode_seconds_excluded']:.1f} s, excluded)")}
+    out.update(host_info())
+    return out
+
+
+def oracle_timings(extra_layers) -> dict:
+    """Oracle times on the small workloads: all BLAS threads and one thread."""
+    res = {}
+    for name, layer, tokens in extra_layers:
+        progress(f"oracle timing {name}")
+        all_t = _oracle_time(layer, tokens=tokens)
+        one_t = _oracle_time(layer, tokens=tokens, single_thread=True)
+        res[name] = {"tokens": all_t["tokens"], "all_threads": all_t, "single_thread": one_t}
+    return res
 
 
 def copy_probe(mib: int):
@@ -342,10 +459,9 @@ def copy_probe(mib: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs the single-GPU layer forward only; --gpus {args.gpus} is not supported "
-              f"(no multi-GPU path is built)", file=sys.stderr)
+        print(f"bench.py measures one GPU: every GPU box here has one, and no multi-GPU path is built; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -356,91 +472,77 @@ def main():
     from routed_expert_moe_amd import binding as B
     from routed_expert_moe_amd import configs, synth
     B.lib()
+    only = set(filter(None, args.only.split(",")))
+    want = (lambda n: not only or n in only)
 
     # ---- prefill: the headline workload
     shape = configs.V3_PREFILL_BF16
-    progress(f"building {shape.name}")
-    layer = synth.make_layer(shape, device="cuda")
-    progress(f"timing {shape.name}")
-    p = Pass(layer)
-    total_ms, up_ms, wall = time_pass(p, args.steps, args.warmup)
-    counts = p.r.counts.cpu().numpy()
-    fig = work_figures(layer, counts)
-    ms = total_ms / args.steps
-    tok_s = shape.T * args.steps / (total_ms / 1e3)
     res = {
         "metric": "MoE-layer tokens/s + % MFMA peak (prefill), % HBM GB/s (decode), 1 MI355X",
-        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
         "config": {"workload": shape.name, "T": shape.T, "dim": shape.dim, "n_routed": shape.n_routed,
                    "n_groups": shape.n_groups, "topk_groups": shape.topk_groups, "top_k": shape.top_k,
                    "n_shared": shape.n_shared, "inter_dim": shape.inter_dim, "score": shape.score,
-                   "route_scale": shape.route_scale, "experts_touched": fig["touched"]},
-        "layer": {"tflops": fig["flops_layer"] / (ms / 1e3) / 1e12,
-                  "mfma_frac": fig["flops_layer"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-                  "gbs": fig["bytes_layer"] / (ms / 1e3) / 1e9,
-                  "hbm_frac": fig["bytes_layer"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
-        "roofline": roofline(fig["flops_up"], fig["bytes_up"], up_ms, measured_traffic("prefill_up"),
-                             "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)"),
-        "wall_s": wall,
+                   "route_scale": shape.route_scale},
     }
-    res["bias_update"] = time_bias_update(p, shape)
-    res["balance_loss"] = time_balance_loss(p, shape)
-    progress("timing the backward")
-    res["backward"] = time_backward(p, shape)
-    del p
-    torch.cuda.empty_cache()
+    head_layer = None
+    if want(shape.name):
+        rep, p = run_workload(shape, args.steps, args.warmup, PEAK_BF16_TFLOPS, "prefill_up",
+                              "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)", keep=True)
+        res["value"] = shape.T * args.steps / (rep["_total_ms"] / 1e3)
+        res["ms_per_step"] = rep["_total_ms"] / args.steps
+        res["wall_s"] = rep.pop("_wall_s")
+        rep.pop("_total_ms")
+        res["config"]["experts_touched"] = rep["experts_touched"]
+        res["step_ms"] = rep["step_ms"]
+        res["stage_ms_median"] = rep["stage_ms_median"]
+        res["layer"] = rep["layer"]
+        res["roofline"] = rep["roofline"]
+        res["bias_update"] = time_bias_update(p, shape)
+        res["balance_loss"] = time_balance_loss(p, shape)
+        if not args.no_backward:
+            progress("timing the backward")
+            res["backward"] = time_backward(p, shape)
+        head_layer = p.layer
+        del p
+        torch.cuda.empty_cache()
 
-    # ---- the same prefill batch in FP8 W8A8 (fp8 weights, activations quantised 1x128)
-    wshape = configs.V3_PREFILL_W8A8
-    progress(f"building {wshape.name}")
-    wlayer = synth.make_layer(wshape, device="cuda")
-    progress(f"timing {wshape.name}")
-    wp = Pass(wlayer)
-    wtotal_ms, wup_ms, _ = time_pass(wp, args.steps, args.warmup)
-    wfig = work_figures(wlayer, wp.r.counts.cpu().numpy())
-    wms = wtotal_ms / args.steps
-    res["prefill_w8a8"] = {
-        "workload": wshape.name, "T": wshape.T,
-        "dtype": "fp8-e4m3 weights (128x128 fp32 scales) x fp8-e4m3 activations (1x128 fp32 scales)",
-        "ms_per_step": wms, "tokens_per_s": wshape.T * args.steps / (wtotal_ms / 1e3),
-        "experts_touched": wfig["touched"],
-        "layer_tflops": wfig["flops_layer"] / (wms / 1e3) / 1e12,
-        "layer_mfma_frac_fp8": wfig["flops_layer"] / (wms / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
-        "roofline": roofline(wfig["flops_up"], wfig["bytes_up"], wup_ms, measured_traffic("w8a8_up"),
-                             "moe_expert_up (fp8 x fp8 grouped GEMM + SwiGLU + h quantisation, gemm_fp8_kernel)",
-                             PEAK_FP8_TFLOPS),
-    }
-    del wp, wlayer
-    torch.cuda.empty_cache()
+    def side(key, shp, steps, peak, traffic_key=None, kernel=None):
+        if not want(shp.name):
+            return
+        rep, _ = run_workload(shp, steps, max(args.warmup, 3), peak, traffic_key, kernel)
+        rep.pop("_wall_s")
+        rep.pop("_total_ms")
+        res[key] = rep
 
-    # ---- decode: 8 tokens, fp8 expert weights
-    dshape = configs.V3_DECODE_FP8
-    progress(f"building {dshape.name}")
-    dlayer = synth.make_layer(dshape, device="cuda")
-    progress(f"timing {dshape.name}")
-    dp = Pass(dlayer)
+    side("prefill_w8a8", configs.V3_PREFILL_W8A8, args.steps, PEAK_FP8_TFLOPS, "w8a8_up",
+         "moe_expert_up (fp8 x fp8 grouped GEMM + SwiGLU + h quantisation, gemm_fp8_kernel)")
     dsteps = args.decode_steps or 10 * args.steps
-    dtotal_ms, dup_ms, _ = time_pass(dp, dsteps, max(args.warmup, 3))
-    dfig = work_figures(dlayer, dp.r.counts.cpu().numpy())
-    dms = dtotal_ms / dsteps
-    res["decode"] = {
-        "workload": dshape.name, "T": dshape.T, "dtype": "fp8-e4m3 weights (128x128 fp32 scales), bf16 act",
-        "steps": dsteps, "ms_per_step": dms, "tokens_per_s": dshape.T * dsteps / (dtotal_ms / 1e3),
-        "experts_touched": dfig["touched"],
-        "layer_gbs": dfig["bytes_layer"] / (dms / 1e3) / 1e9,
-        "layer_hbm_frac": dfig["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
-        "roofline": roofline(dfig["flops_up"], dfig["bytes_up"], dup_ms, measured_traffic("decode_up"),
-                             "moe_expert_up (fp8 weight-streaming gate/up + SwiGLU, gemm_skinny_kernel)"),
-    }
-    del dp, dlayer
-    torch.cuda.empty_cache()
-    progress("timing the expert-parallel share")
-    res["ep_shard"] = time_ep_shard(args)
-    if not args.no_cpu_baseline:
+    side("decode", configs.V3_DECODE_FP8, dsteps, PEAK_BF16_TFLOPS, "decode_up",
+         "moe_expert_up (fp8 weight-streaming gate/up + SwiGLU, gemm_skinny_kernel)")
+    side("v2_T4096", configs.V2_BF16, args.steps, PEAK_BF16_TFLOPS, None,
+         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")
+    side("v2lite_T512", configs.V2_LITE_BF16, 5 * args.steps, PEAK_BF16_TFLOPS, None,
+         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")
+    side("tiny_f32", configs.TINY_F32, 10 * args.steps, PEAK_F32_TFLOPS, None,
+         "moe_expert_up (fp32 SIMT grouped GEMM + SwiGLU, gemm_f32_kernel)")
+    side("ep_shard", configs.V3_EP_SHARD_BF16, args.steps, PEAK_BF16_TFLOPS, None,
+         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")
+    if "ep_shard" in res:
+        res["ep_shard"]["what"] = ("one GPU's expert-parallel share of v3_prefill_bf16_T8192 (a local routing "
+                                   "of the dispatched tokens stands in for the global gate; no collectives)")
+
+    if not args.no_cpu_baseline and head_layer is not None:
         progress("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(layer, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(head_layer, args.cpu_tokens)
+        del head_layer
+        torch.cuda.empty_cache()
+        small = [("tiny_f32", synth.make_layer(configs.TINY_F32, device="cpu"), None),
+                 ("v3_decode_fp8_T8", synth.make_layer(configs.V3_DECODE_FP8, device="cuda"), None)]
+        res["oracle_timing"] = oracle_timings(small)
+        del small
     print(json.dumps(res), flush=True)
 
 
