@@ -8,6 +8,8 @@
 
 #include "backward.hpp"
 
+#include <algorithm>
+
 namespace moe {
 int64_t permute_scratch_ints(int64_t P, int E);
 }
@@ -348,6 +350,12 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
       case PATH_F32: return launch_gemm_f32(segs, nseg, p.tile_m, epi, st);
       case PATH_FP8: return launch_gemm_fp8(segs, nseg, epi, st);
       case PATH_MFMA:
+        if (r.tile_m == 128 && gemm_expert_supported(segs, nseg)) {
+          const int32_t *nu = r.scratch + permute_units_offset(T * c.top_k, c.n_routed);
+          const int64_t a_bytes = segs == up ? T * D * 2
+                                             : std::max<int64_t>(static_cast<int64_t>(r.max_rows) * I, T * SI) * 2;
+          return launch_gemm_expert(segs, nseg, epi, nu + 4, nu, a_bytes, st);
+        }
         if (gemm_mfma2_supported(segs, nseg)) return launch_gemm_mfma2(segs, nseg, epi, false, st);
         return launch_gemm_mfma(segs, nseg, p.tile_m, epi, false, st);
       default: return launch_gemm_skinny(segs, nseg, epi, fp8, false, st);

@@ -99,6 +99,18 @@ struct Segment {
 
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1 };
 
+// The forward expert GEMM takes an expert's rows in chunks of up to kChunkTiles
+// 128-row tiles; a chunk of t tiles runs as one tile of 128 * chunk_units(t) rows
+// (1, 2 or 4 units).
+constexpr int kChunkTiles = 2;
+__host__ __device__ constexpr int chunk_units(int tiles) { return tiles <= 1 ? 1 : tiles <= 2 ? 2 : 4; }
+// 128-row units of n128 tiles cut into chunks
+__host__ __device__ constexpr int units_of_tiles(int n128) {
+  return n128 <= 0 ? 0
+                   : chunk_units(kChunkTiles) * ((n128 - 1) / kChunkTiles) +
+                         chunk_units(n128 - kChunkTiles * ((n128 - 1) / kChunkTiles));
+}
+
 // plan chosen for (cfg, T)
 enum Path { PATH_F32 = 0, PATH_MFMA = 1, PATH_SKINNY = 2, PATH_FP8 = 3 };
 struct Plan {
@@ -142,6 +154,14 @@ hipError_t launch_gemm_mfma2(const Segment *segs, int nseg, Epilogue epi, bool o
 // per row), on the prefill GEMM's tiling; routed segments need 128-row routing tiles
 bool gemm_mfma2_bt_supported(const Segment *segs, int nseg);
 hipError_t launch_gemm_mfma2_bt(const Segment *segs, int nseg, hipStream_t st);
+// The forward expert GEMMs on expert-sized tiles: segs[0] routed, its rows cut
+// into the chunk table moe_permute writes with 128-row tiles (units, n_units);
+// segs[1] (optional) dense.  a_bytes_max bounds every A matrix's size in bytes.
+bool gemm_expert_supported(const Segment *segs, int nseg);
+hipError_t launch_gemm_expert(const Segment *segs, int nseg, Epilogue epi, const int32_t *units,
+                              const int32_t *n_units, int64_t a_bytes_max, hipStream_t st);
+// where the chunk table sits in a routing buffer's scratch (in int32 entries)
+int64_t permute_units_offset(int64_t P, int E);
 hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool w_fp8,
                               bool out_f32, hipStream_t st);
 

@@ -64,10 +64,7 @@ namespace moe {
 namespace {
 
 constexpr int BM = 128, BN = 512, BK = 64;
-#ifndef MOE_MFMA2_WAVES
-#define MOE_MFMA2_WAVES 8
-#endif
-constexpr int kWaves = MOE_MFMA2_WAVES;                 // wavefronts per workgroup, side by side
+constexpr int kWaves = 8;                               // wavefronts per workgroup, side by side
 constexpr int kThreads = 64 * kWaves;
 constexpr int NJ = BN / kWaves / 32;                    // 32-row B sub-tiles per wavefront
 constexpr int kStages = 2;

@@ -13,6 +13,14 @@
 //   3. scatter: row = expert_off[e] + base[blk][e] + rank.
 // With a single count workgroup (T*K <= 2048) the three phases run in one
 // launch that keeps its intermediate tables in LDS.  Every value is computed without atomics, so the result is unique.
+//
+// With 128-row tiles the scan also lists each expert's row chunks for the
+// prefill GEMM (write_units below): an expert's rows are cut into chunks of up
+// to kChunkTiles 128-row tiles, and a chunk of n tiles is computed as one tile
+// of 128*mw rows with mw = chunk_units(n) (1, 2, 4, 4 for n = 1, 2, 3, 4), so
+// that one workgroup holds every row of the chunk and reads each weight row
+// once.  The table has one entry per 128-row unit of mw (a chunk of mw units),
+// in expert order.
 #include "common.hpp"
 
 namespace moe {
@@ -33,7 +41,61 @@ struct PermArgs {
   int32_t *counts, *expert_off, *sorted_pair, *pair_row, *tile_expert, *tile_row, *n_tiles;
   int32_t *local_rank;  // [P]
   int32_t *hist;        // [nblk][E]
+  int32_t *units;       // [max units][4] chunk table (TM == 128), or nullptr
+  int32_t *n_units;     // [1]
 };
+
+
+// the chunk entries of expert e: rows [off, off + padded), `cnt` of them real;
+// entry {first row, end of its real rows, expert, (mw << 8) | unit within the chunk}
+__device__ void write_units(const PermArgs &a, int e, int off, int cnt, int padded, int u0) {
+  const int n128 = padded / 128;
+  const int nch = (n128 + kChunkTiles - 1) / kChunkTiles;
+  int u = u0;
+  for (int c = 0; c < nch; ++c) {
+    const int tiles = min(kChunkTiles, n128 - kChunkTiles * c);
+    const int mw = chunk_units(tiles);
+    const int row0 = off + 128 * kChunkTiles * c;
+    const int real_end = min(row0 + 128 * tiles, off + cnt);
+    for (int j = 0; j < mw; ++j, ++u) {
+      int32_t *d = a.units + 4 * static_cast<int64_t>(u);
+      d[0] = row0;
+      d[1] = real_end;
+      d[2] = e;
+      d[3] = (mw << 8) | j;
+    }
+  }
+}
+
+// inclusive Hillis-Steele scan of v[0, kMaxE) in LDS, two entries per thread (kPermThreads)
+__device__ void scan_lds(int *v) {
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    int v0 = 0, v1 = 0;
+    const int i0 = threadIdx.x, i1 = threadIdx.x + kPermThreads;
+    if (i0 >= off) v0 = v[i0 - off];
+    if (i1 >= off) v1 = v[i1 - off];
+    __syncthreads();
+    v[i0] += v0;
+    v[i1] += v1;
+    __syncthreads();
+  }
+}
+
+// the chunk table from counts and padded ends (TM == 128); s_u is LDS scratch of kMaxE
+__device__ void build_units(const PermArgs &a, const int *s_cnt_e, const int *s_end, int *s_u) {
+  for (int e = threadIdx.x; e < kMaxE; e += kPermThreads) {
+    const int start = e > 0 ? s_end[e - 1] : 0;
+    s_u[e] = e < a.E ? units_of_tiles((s_end[e] - start) / 128) : 0;
+  }
+  __syncthreads();
+  scan_lds(s_u);
+  for (int e = threadIdx.x; e < a.E; e += kPermThreads) {
+    const int start = e > 0 ? s_end[e - 1] : 0;
+    const int u0 = e > 0 ? s_u[e - 1] : 0;
+    write_units(a, e, start, s_cnt_e[e], s_end[e] - start, u0);
+  }
+  if (threadIdx.x == 0) *a.n_units = s_u[kMaxE - 1];
+}
 
 __device__ __forceinline__ int expert_of(const PermArgs &a, int64_t p) {
   if (p >= a.P) return -1;
@@ -90,7 +152,7 @@ __device__ void count_block(const PermArgs &a, int blk, int (*s_cnt)[kMaxE]) {
 }
 
 // phase 2, one workgroup of kPermThreads
-__device__ void scan_all(const PermArgs &a, int *s_pad) {
+__device__ void scan_all(const PermArgs &a, int *s_pad, int *s_cnt_e, int *s_u) {
   for (int e = threadIdx.x; e < a.E; e += kPermThreads) {
     int run = 0;
     for (int b = 0; b < a.nblk; ++b) {
@@ -100,21 +162,12 @@ __device__ void scan_all(const PermArgs &a, int *s_pad) {
       run += v;
     }
     a.counts[e] = run;
+    s_cnt_e[e] = run;
     s_pad[e] = (run + a.TM - 1) / a.TM * a.TM;
   }
   for (int e = a.E + threadIdx.x; e < kMaxE; e += kPermThreads) s_pad[e] = 0;
   __syncthreads();
-  // inclusive Hillis-Steele scan over kMaxE entries, two per thread
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    int v0 = 0, v1 = 0;
-    const int i0 = threadIdx.x, i1 = threadIdx.x + kPermThreads;
-    if (i0 >= off) v0 = s_pad[i0 - off];
-    if (i1 >= off) v1 = s_pad[i1 - off];
-    __syncthreads();
-    s_pad[i0] += v0;
-    s_pad[i1] += v1;
-    __syncthreads();
-  }
+  scan_lds(s_pad);
   for (int e = threadIdx.x; e < a.E; e += kPermThreads) {
     const int end = s_pad[e];
     const int cnt = a.counts[e];
@@ -131,6 +184,7 @@ __device__ void scan_all(const PermArgs &a, int *s_pad) {
     a.expert_off[a.E] = s_pad[a.E - 1];
     *a.n_tiles = s_pad[a.E - 1] / a.TM;
   }
+  if (a.units != nullptr) build_units(a, s_cnt_e, s_pad, s_u);
 }
 
 // phase 3 for pairs [p0, min(p1, P))
@@ -156,7 +210,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_count_kernel(PermArgs a)
 
 __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(PermArgs a) {
   __shared__ int s_pad[kMaxE];
-  scan_all(a, s_pad);
+  __shared__ int s_cnt_e[kMaxE];
+  __shared__ int s_u[kMaxE];
+  scan_all(a, s_pad, s_cnt_e, s_u);
 }
 
 __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(PermArgs a) {
@@ -172,6 +228,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(PermArgs a)
   __shared__ int s_tot[kMaxE];               // pairs per expert
   __shared__ int s_end[kMaxE];               // padded sizes, then inclusive padded ends
   __shared__ int s_rank[kPairsPerBlock];     // rank among the wavefront's pairs of one expert
+  __shared__ int s_u[kMaxE];                 // chunk units per expert, then their inclusive scan
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int i = threadIdx.x; i < kPermWaves * kMaxE; i += kPermThreads) (&s_cnt[0][0])[i] = 0;
   constexpr int kChunks = kPairsPerWave / 64;
@@ -223,16 +280,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(PermArgs a)
     s_end[e] = (run + a.TM - 1) / a.TM * a.TM;
   }
   __syncthreads();
-  for (int off = 1; off < kMaxE; off <<= 1) {   // inclusive scan, two entries per thread
-    int v0 = 0, v1 = 0;
-    const int i0 = threadIdx.x, i1 = threadIdx.x + kPermThreads;
-    if (i0 >= off) v0 = s_end[i0 - off];
-    if (i1 >= off) v1 = s_end[i1 - off];
-    __syncthreads();
-    s_end[i0] += v0;
-    s_end[i1] += v1;
-    __syncthreads();
-  }
+  scan_lds(s_end);
   for (int e = threadIdx.x; e < a.E; e += kPermThreads) {
     const int end = s_end[e];
     const int start = e > 0 ? s_end[e - 1] : 0;
@@ -247,6 +295,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(PermArgs a)
     a.expert_off[a.E] = s_end[a.E - 1];
     *a.n_tiles = s_end[a.E - 1] / a.TM;
   }
+  if (a.units != nullptr) build_units(a, s_tot, s_end, s_u);
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int64_t p = base + c * 64 + lane;
@@ -266,9 +315,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(PermArgs a)
 
 }  // namespace
 
-int64_t permute_scratch_ints(int64_t P, int E) {
+// scratch of a routing buffer: local ranks [P], histograms [nblk][E], then the
+// chunk table: n_units (padded to 4 ints) and [max units][4] entries.  An
+// expert of n 128-row tiles has at most n + 1 units, and sum n <= P/128 + E.
+int64_t permute_units_offset(int64_t P, int E) {
   const int64_t nblk = (P + kPairsPerBlock - 1) / kPairsPerBlock;
-  return P + nblk * E;
+  return (P + nblk * E + 3) / 4 * 4;   // 16-byte aligned entries
+}
+int64_t permute_max_units(int64_t P, int E) { return P / 128 + 2 * static_cast<int64_t>(E) + 2; }
+int64_t permute_scratch_ints(int64_t P, int E) {
+  return permute_units_offset(P, E) + 4 + 4 * permute_max_units(P, E);
 }
 
 hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_idx,
@@ -288,6 +344,13 @@ hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_
   a.n_tiles = r.n_tiles;
   a.local_rank = r.scratch;
   a.hist = r.scratch + a.P;
+  a.units = nullptr;
+  a.n_units = nullptr;
+  if (a.TM == 128) {
+    int32_t *u = r.scratch + permute_units_offset(a.P, a.E);
+    a.n_units = u;
+    a.units = u + 4;
+  }
   if (a.nblk == 1) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, st, a);
     return hipGetLastError();
