@@ -111,7 +111,7 @@ typedef struct moe_weights {
  * Build it with moe_routing_init over one caller buffer of moe_routing_size bytes. */
 typedef struct moe_routing {
   int32_t tile_m;        /* host: rows per expert tile (chosen by the library for (cfg, T)) */
-  int32_t max_rows;      /* host: capacity in rows = T*K + E*(tile_m-1), rounded up to tile_m */
+  int32_t max_rows;      /* host: capacity in rows = T*K + min(T*K, E)*(tile_m-1), rounded up to tile_m */
   int32_t max_tiles;     /* host: capacity of the tile lists = max_rows / tile_m */
   int32_t pad_;
   int32_t *counts;       /* [E]          pairs routed to each expert */

@@ -64,7 +64,10 @@ RoutingLayout routing_layout(const moe_config &c, int64_t T) {
   const Plan p = plan_for(c, T);
   L.tile_m = p.tile_m;
   L.P = T * c.top_k;
-  L.max_rows = static_cast<int64_t>(round_up(static_cast<size_t>(L.P + static_cast<int64_t>(c.n_routed) * (p.tile_m - 1)), p.tile_m));
+  // rows in use: every expert that received a pair pads to a multiple of tile_m, and at
+  // most min(P, E) experts receive one
+  const int64_t busy = std::min<int64_t>(L.P, c.n_routed);
+  L.max_rows = static_cast<int64_t>(round_up(static_cast<size_t>(L.P + busy * (p.tile_m - 1)), p.tile_m));
   L.max_tiles = L.max_rows / p.tile_m;
   size_t o = 0;
   auto take = [&](size_t bytes) {
