@@ -229,6 +229,19 @@ moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const mo
                        void *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* The whole layer with no allocation anywhere, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and validation as
+ * moe_forward, without `ws`: the workspace is a 64 MiB device array inside this
+ * library (each GPU the library runs on holds its own copy until the process
+ * ends).  Layers whose moe_workspace_size exceeds 64 MiB (a V3-shaped layer up
+ * to a few dozen tokens, larger T for smaller layers) return MOE_ERR_WORKSPACE
+ * before any launch.  The array keeps the last call's contents, which no call
+ * reads before writing; every call on one GPU uses the same array, so calls that
+ * overlap on one GPU (on other streams or from other threads) race. */
+moe_status moe_forward_static(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                              void *out, int32_t *topk_idx, float *topk_w, void *stream);
+
 /* Auxiliary-loss-free load balancing, one step (DeepSeek-V3 notes page,
  * "V3 improvement 1": b_i follows each expert's load at speed gamma; DeepSeek-R1
  * analysis page, MoE hyper-parameters paragraph: an overloaded expert's bias is

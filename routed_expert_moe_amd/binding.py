@@ -68,7 +68,7 @@ EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspa
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update",
             "moe_quant_act", "moe_balance_loss", "moe_balance_loss_workspace_size",
-            "moe_backward", "moe_backward_workspace_size")
+            "moe_backward", "moe_backward_workspace_size", "moe_forward_static")
 
 _lib = None
 
@@ -98,6 +98,7 @@ def lib():
                             P, P, P, P, P],
         "moe_combine": [cfgp, I64, P, P, P, ctypes.POINTER(moe_routing), P, P, P],
         "moe_forward": [cfgp, I64, P, ctypes.POINTER(moe_weights), P, P, P, P, SZ, P],
+        "moe_forward_static": [cfgp, I64, P, ctypes.POINTER(moe_weights), P, P, P, P],
         "moe_bias_update": [cfgp, I64, ctypes.POINTER(moe_routing), ctypes.c_float, P, P],
         "moe_quant_act": [cfgp, I64, P, ctypes.POINTER(moe_routing), P],
         "moe_balance_loss": [cfgp, I64, ctypes.c_int32, P, P, ctypes.c_float, P, ctypes.c_size_t, P, P],
@@ -329,6 +330,12 @@ def moe_forward(cfg: moe_config, T: int, x, weights: moe_weights, out, topk_idx=
     _check(lib().moe_forward(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(weights), _ptr(out),
                              _ptr(topk_idx), _ptr(topk_w), _ptr(ws), 0 if ws is None else ws.numel(),
                              _stream(stream)))
+
+
+def moe_forward_static(cfg: moe_config, T: int, x, weights: moe_weights, out, topk_idx=None, topk_w=None,
+                       stream=None) -> None:
+    _check(lib().moe_forward_static(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(weights), _ptr(out),
+                                    _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
 
 
 # ---- convenience: one layer's state on the device ----------------------------------

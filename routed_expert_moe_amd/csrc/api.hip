@@ -182,6 +182,18 @@ moe_status check_bias(const moe_config &c, const float *bias) {
   return MOE_OK;
 }
 
+}  // namespace
+
+// the thread-local message moe_last_error returns, for entry points in other sources
+namespace moe {
+moe_status set_error(moe_status s, const char *msg) {
+  snprintf(g_err, sizeof(g_err), "%s", msg);
+  return s;
+}
+}  // namespace moe
+
+namespace {
+
 #define MOE_TRY(expr)            \
   do {                           \
     const moe_status s_ = (expr); \

@@ -160,6 +160,8 @@ hipError_t launch_gemm_mfma2_bt(const Segment *segs, int nseg, hipStream_t st);
 bool gemm_expert_supported(const Segment *segs, int nseg);
 hipError_t launch_gemm_expert(const Segment *segs, int nseg, Epilogue epi, const int32_t *units,
                               const int32_t *n_units, int64_t a_bytes_max, hipStream_t st);
+// sets the thread-local message moe_last_error() returns; returns s
+moe_status set_error(moe_status s, const char *msg);
 // where the chunk table sits in a routing buffer's scratch (in int32 entries)
 int64_t permute_units_offset(int64_t P, int E);
 hipError_t launch_gemm_skinny(const Segment *segs, int nseg, Epilogue epi, bool w_fp8,

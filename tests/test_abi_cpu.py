@@ -212,3 +212,21 @@ def test_backward_validates_before_launch():
                           fake, ctypes.byref(g), None, 0, None) == B.MOE_OK
     # the workspace grows with T and holds the 128-row tile lists, fp32 a/c, dh, dx per routed row
     assert B.moe_backward_workspace_size(c, 2 * T) > need
+
+
+def test_static_forward_rejects_layers_beyond_its_scratch():
+    """moe_forward_static checks its workspace need against the static array on the
+    host, before any device call: the V3 prefill batch needs far more than 64 MiB."""
+    import torch
+    shape = configs.V3_PREFILL_BF16
+    cfg = B.config_of(shape)
+    assert B.moe_workspace_size(cfg, shape.T) > 64 << 20
+    x = torch.zeros(16)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_static(cfg, shape.T, x, B.moe_weights(), x, stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+    assert "static" in B.lib().moe_last_error().decode()
+    bad = B.config_of(shape.with_(n_groups=3))
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_static(bad, 8, x, B.moe_weights(), x, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
