@@ -39,24 +39,36 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 
-// 128-row tiles over each expert's rows [off[e], off[e+1]) (one thread)
-__global__ void bwd_tiles_kernel(const int32_t *__restrict__ expert_off, int E, int32_t *tile_row,
-                                 int32_t *tile_expert, int32_t *tile_end, int32_t *tile_first,
-                                 int32_t *n_tiles) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int n = 0;
-  for (int e = 0; e < E; ++e) {
-    const int a = expert_off[e], b = expert_off[e + 1];
-    const int first = n;
-    for (int r = a; r < b; r += 128) {
-      tile_row[n] = r;
-      tile_expert[n] = e;
-      tile_end[n] = b;
-      tile_first[n] = first;
-      ++n;
-    }
+// 128-row tiles over each expert's rows [off[e], off[e+1]): one thread per expert
+// counts its tiles, an exclusive scan in LDS places them, each thread writes its own
+constexpr int kTilesThreads = 512;   // >= the largest supported n_routed
+__global__ __launch_bounds__(kTilesThreads) void bwd_tiles_kernel(
+    const int32_t *__restrict__ expert_off, int E, int32_t *tile_row, int32_t *tile_expert,
+    int32_t *tile_end, int32_t *tile_first, int32_t *n_tiles) {
+  __shared__ int s_n[kTilesThreads];
+  const int e = threadIdx.x;
+  int a = 0, b = 0;
+  if (e < E) {
+    a = expert_off[e];
+    b = expert_off[e + 1];
   }
-  *n_tiles = n;
+  const int cnt = (b - a + 127) / 128;
+  s_n[e] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kTilesThreads; off <<= 1) {   // inclusive scan
+    const int v = e >= off ? s_n[e - off] : 0;
+    __syncthreads();
+    s_n[e] += v;
+    __syncthreads();
+  }
+  const int first = s_n[e] - cnt;
+  for (int j = 0; j < cnt; ++j) {
+    tile_row[first + j] = a + 128 * j;
+    tile_expert[first + j] = e;
+    tile_end[first + j] = b;
+    tile_first[first + j] = first;
+  }
+  if (e == kTilesThreads - 1) *n_tiles = s_n[e];
 }
 
 // one workgroup (256 threads) per used row of the expert-sorted layout
@@ -230,7 +242,8 @@ __global__ __launch_bounds__(256) void dx_final_kernel(
 
 hipError_t launch_bwd_tiles(const int32_t *expert_off, int E, int32_t *tile_row, int32_t *tile_expert,
                             int32_t *tile_end, int32_t *tile_first, int32_t *n_tiles, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(64), 0, st, expert_off, E, tile_row, tile_expert,
+  if (E > kTilesThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(kTilesThreads), 0, st, expert_off, E, tile_row, tile_expert,
                      tile_end, tile_first, n_tiles);
   return hipGetLastError();
 }
