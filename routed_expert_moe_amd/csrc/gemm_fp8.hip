@@ -239,9 +239,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
     float sa[4], c_prev[4][NJ];
     auto kloop = [&](auto nbc) {
       constexpr int NB = decltype(nbc)::value;
-      // branch-free K loop: block 0's scales seed c_prev (the first rescale multiplies
-      // zeros by one), and the last step prefetches block nk-1 again into the stage
-      // its predecessor has finished with
+      // block 0's scales seed c_prev (the first rescale multiplies zeros by one); the
+      // last step issues no loads (its scale reads fetch block nk-1 again, harmlessly)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sa[i] = ascale(i, 0);
 #pragma unroll
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
         float sa_next[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sa_next[i] = ascale(i, kn);
-        issue(kn);
+        if (kt + 1 < nk) issue(kn);   // the other stage: every wavefront finished reading it
         // rescale the running sums from block kt-1's scale to block kt's
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -305,7 +304,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
       case 3: kloop(std::integral_constant<int, 3>{}); break;
       default: kloop(std::integral_constant<int, 4>{}); break;
     }
-    __syncthreads();   // all waves done with both stages
+    // every load has landed (the last step issued none) and all waves are done with both stages
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
 
     // ---- epilogue.  acc[i][j][4g + t] * c_prev[i][j] is C[row i*32 + l32][col j*32 + 8g + 4*khalf + t].
     if (EPI == EPI_SWIGLU) {
