@@ -50,18 +50,22 @@ PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector)
 # reported as null once that source has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
-    "prefill_up": {"sources": ("gemm_mfma2.hip", "common.hpp"),
-                   "sha256": "5ea999a830e876989880a17369a4bd9983bda3dcbcad28bb01a761a5f0239d24",
-                   "fetch_kib": 14221656, "write_kib": 362496,
-                   "profile": "profiles/gemm_mfma2_gate_up_v3_prefill_T8192_counters.md"},
+    "prefill_up": {"sources": ("gemm_expert.hip", "common.hpp"),
+                   "sha256": "f50e9a127ce5dac484af965382936099a446417d6176d4733e97cfe4262e16f3",
+                   "fetch_kib": 12247822, "write_kib": 294912,
+                   "profile": "profiles/gemm_expert_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
-                  "sha256": "59dfca776df8586e4571956ac60856b9efcde10db974a41401e24df0a446861b",
-                  "fetch_kib": 847312, "write_kib": 3744,
+                  "sha256": "a32331a6878bd065219e09a9d486a0c92876bb9eaa722f78d44c9a91491367e2",
+                  "fetch_kib": 775590, "write_kib": 3424,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
-                "sha256": "c5818489c1ece2dde52e881ed7511c33516576c68d06cbbbbf1a52b4dd3c85ca",
-                "fetch_kib": 9022782, "write_kib": 195868,
+                "sha256": "5cd7287ca997c0267b2af99cd3bea93e6062a6eeb1b9ce27a18d7db8f1cc44b1",
+                "fetch_kib": 8314388, "write_kib": 194265,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
+    "v2_up": {"sources": ("gemm_expert.hip", "common.hpp"),
+              "sha256": "f50e9a127ce5dac484af965382936099a446417d6176d4733e97cfe4262e16f3",
+              "fetch_kib": 3105696, "write_kib": 98304,
+              "profile": "profiles/gemm_expert_gate_up_v2_T4096_counters.md"},
 }
 
 
@@ -490,7 +494,7 @@ def main():
     head_layer = None
     if want(shape.name):
         rep, p = run_workload(shape, args.steps, args.warmup, PEAK_BF16_TFLOPS, "prefill_up",
-                              "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)", keep=True)
+                              "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_expert_kernel)", keep=True)
         res["value"] = shape.T * args.steps / (rep["_total_ms"] / 1e3)
         res["ms_per_step"] = rep["_total_ms"] / args.steps
         res["wall_s"] = rep.pop("_wall_s")
@@ -522,14 +526,14 @@ def main():
     dsteps = args.decode_steps or 10 * args.steps
     side("decode", configs.V3_DECODE_FP8, dsteps, PEAK_BF16_TFLOPS, "decode_up",
          "moe_expert_up (fp8 weight-streaming gate/up + SwiGLU, gemm_skinny_kernel)")
-    side("v2_T4096", configs.V2_BF16, args.steps, PEAK_BF16_TFLOPS, None,
-         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")
+    side("v2_T4096", configs.V2_BF16, args.steps, PEAK_BF16_TFLOPS, "v2_up",
+         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_expert_kernel)")
     side("v2lite_T512", configs.V2_LITE_BF16, 5 * args.steps, PEAK_BF16_TFLOPS, None,
-         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")
+         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_expert_kernel)")
     side("tiny_f32", configs.TINY_F32, 10 * args.steps, PEAK_F32_TFLOPS, None,
          "moe_expert_up (fp32 SIMT grouped GEMM + SwiGLU, gemm_f32_kernel)")
     side("ep_shard", configs.V3_EP_SHARD_BF16, args.steps, PEAK_BF16_TFLOPS, None,
-         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_mfma2_kernel)")
+         "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_expert_kernel)")
     if "ep_shard" in res:
         res["ep_shard"]["what"] = ("one GPU's expert-parallel share of v3_prefill_bf16_T8192 (a local routing "
                                    "of the dispatched tokens stands in for the global gate; no collectives)")
