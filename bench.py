@@ -113,7 +113,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=0, help="default: 10x --steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=6144,
                     help="tokens of the headline workload the CPU oracle is timed on")
     ap.add_argument("--only", default="",
                     help="comma-separated workloads to time (default: all); names as in the JSON")

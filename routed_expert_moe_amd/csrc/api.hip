@@ -243,12 +243,12 @@ moe_status do_gate(const moe_config &c, int64_t T, const void *x, const void *w_
     s.n_tiles_host = static_cast<int32_t>((T + kF32TileM - 1) / kF32TileM);
     e = launch_gemm_f32(&s, 1, kF32TileM, EPI_STORE, st);
   } else if (T >= 64) {
-    s.n_tiles_host = static_cast<int32_t>((T + kMfmaTileM - 1) / kMfmaTileM);
-    // with few experts the 512-wide tile of the prefill GEMM leaves most CUs idle
-    // (one work item per 128 tokens); 128 x 128 tiles give twice the items or more
-    const bool wide = c.n_routed > 256 && gemm_mfma2_supported(&s, 1);
-    e = wide ? launch_gemm_mfma2(&s, 1, EPI_STORE, true, st)
-             : launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
+    if (gate_logits_supported(T, c.n_routed, c.dim)) {
+      e = launch_gate_logits(T, c.n_routed, c.dim, x, w_gate, logits, st);
+    } else {
+      s.n_tiles_host = static_cast<int32_t>((T + kMfmaTileM - 1) / kMfmaTileM);
+      e = launch_gemm_mfma(&s, 1, kMfmaTileM, EPI_STORE, true, st);
+    }
   } else {
     e = launch_gate_logits_gemv(c, T, x, w_gate, logits, st);
   }
