@@ -51,21 +51,25 @@ PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector)
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-                   "sha256": "f50e9a127ce5dac484af965382936099a446417d6176d4733e97cfe4262e16f3",
+                   "sha256": "ceea4922f60c05b526ebf70d1b7c9dffb6737db3104f090d1d9d89c21e123dac",
                    "fetch_kib": 12247822, "write_kib": 294912,
                    "profile": "profiles/gemm_expert_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
-                  "sha256": "a32331a6878bd065219e09a9d486a0c92876bb9eaa722f78d44c9a91491367e2",
+                  "sha256": "ae531b336c9b90738d445d9b97821a3c98dab4beef5d25e511f13147ef4a8e5c",
                   "fetch_kib": 775590, "write_kib": 3424,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
-                "sha256": "5cd7287ca997c0267b2af99cd3bea93e6062a6eeb1b9ce27a18d7db8f1cc44b1",
+                "sha256": "b6d082a256501a24d4d3324f5f15a88789201da6147954e4fe05d7b45f527438",
                 "fetch_kib": 8314388, "write_kib": 194265,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
     "v2_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-              "sha256": "f50e9a127ce5dac484af965382936099a446417d6176d4733e97cfe4262e16f3",
+              "sha256": "ceea4922f60c05b526ebf70d1b7c9dffb6737db3104f090d1d9d89c21e123dac",
               "fetch_kib": 3105696, "write_kib": 98304,
               "profile": "profiles/gemm_expert_gate_up_v2_T4096_counters.md"},
+    "ep_up": {"sources": ("gemm_expert.hip", "common.hpp"),
+              "sha256": "ceea4922f60c05b526ebf70d1b7c9dffb6737db3104f090d1d9d89c21e123dac",
+              "fetch_kib": 1280384, "write_kib": 32768,
+              "profile": "profiles/gemm_expert_gate_up_v3_ep_shard_T4096_E32_counters.md"},
 }
 
 
@@ -532,7 +536,7 @@ def main():
          "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_expert_kernel)")
     side("tiny_f32", configs.TINY_F32, 10 * args.steps, PEAK_F32_TFLOPS, None,
          "moe_expert_up (fp32 SIMT grouped GEMM + SwiGLU, gemm_f32_kernel)")
-    side("ep_shard", configs.V3_EP_SHARD_BF16, args.steps, PEAK_BF16_TFLOPS, None,
+    side("ep_shard", configs.V3_EP_SHARD_BF16, args.steps, PEAK_BF16_TFLOPS, "ep_up",
          "moe_expert_up (gate/up grouped GEMM + SwiGLU, gemm_expert_kernel)")
     if "ep_shard" in res:
         res["ep_shard"]["what"] = ("one GPU's expert-parallel share of v3_prefill_bf16_T8192 (a local routing "
