@@ -12,9 +12,11 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 per block pair (hardware scales fixed at 1).
 //
 // Block scales: each accumulator holds the running sum divided by the current
-// block's combined scale c_b = sa[row][b] * sw[col block][b]; moving to block b
-// multiplies it by c_{b-1} / c_b before the block's MFMAs, and the epilogue
-// multiplies by the last c.  That is exact up to one fp32 rounding per block.
+// block's combined scale c_b = sa[row][b] * sw[col block][b] (the activation
+// scale raised to at least 2^-80 of the row's largest so far, so the ratio below
+// stays finite); moving to block b multiplies it by c_{b-1} / c_b before the
+// block's MFMAs, and the epilogue multiplies by the last c.  That is exact up to
+// one fp32 rounding per block.
 //
 // Routed tiles skip the MFMAs, fragment reads and rescaling of 32-row blocks
 // that hold only padding (an expert's last tile); those rows come out as zeros.
@@ -45,6 +47,13 @@ constexpr int kBLoads = BN * kRowBytes / 1024 / kWaves; // 8
 constexpr int kLoads = kALoads + kBLoads;
 constexpr int kScaleRegs = 2;                           // weight scales of up to 128 K blocks
 constexpr float kE4m3Max = 448.0f;
+// Moving the running sums from a block scale c_prev to a much smaller c multiplies them by
+// c_prev / c, which for a block of tiny activations (amax ~ 1e-30) after a large one could
+// overflow fp32.  So a row's activation scale is raised to at least 2^-80 times the largest
+// it had in the earlier blocks: the sums then stay within 2^80 * 448^2 * K * (weight scale
+// spread) of the largest term, far below the fp32 range, and a raised block contributes at
+// most 2^-80 of what the row's largest block can.
+constexpr float kRelFloor = 0x1p-80f;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
@@ -236,13 +245,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
     }
     nblk = uniform(nblk);
 
-    float sa[4], c_prev[4][NJ];
+    float sa[4], sa_max[4], c_prev[4][NJ];
     auto kloop = [&](auto nbc) {
       constexpr int NB = decltype(nbc)::value;
       // block 0's scales seed c_prev (the first rescale multiplies zeros by one); the
       // last step issues no loads (its scale reads fetch block nk-1 again, harmlessly)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = ascale(i, 0);
+      for (int i = 0; i < 4; ++i) sa[i] = sa_max[i] = ascale(i, 0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const float sw0 = wscale(j, 0);
@@ -262,12 +271,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
         for (int i = 0; i < 4; ++i) sa_next[i] = ascale(i, kn);
         if (kt + 1 < nk) issue(kn);   // the other stage: every wavefront finished reading it
         // rescale the running sums from block kt-1's scale to block kt's
+        float sae[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sae[i] = fmaxf(sa[i], sa_max[i] * kRelFloor);
+          sa_max[i] = fmaxf(sa_max[i], sa[i]);
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const float sw = wscale(j, kt);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float c = sa[i] * sw;
+            const float c = sae[i] * sw;
             if (i >= NB) {   // padding block: keep the scale bookkeeping only
               c_prev[i][j] = c;
               continue;

@@ -318,6 +318,7 @@ def _blocky_layer():
             x[t, nb] *= 1e-30 / x[t, nb].abs().max()
         elif kind == 4 and t % 12 == 4:      # a whole row of tiny blocks
             x[t] *= 1e-30 / x[t].abs().max()
+
     x[T - 1] = 0.0                           # one all-zero token
     layer.x = x.to(torch.bfloat16).cuda()
     return layer
@@ -328,5 +329,23 @@ def test_w8a8_zero_and_tiny_activation_blocks():
     xb = to_f64(layer.x).astype(np.float32).reshape(layer.shape.T, -1, 128)
     amax = np.abs(xb).max(axis=2)
     assert (amax == 0).sum() > 20 and ((amax > 0) & (amax <= 1e-30)).sum() > 20
+    _check_h_codes(layer)
+    _check(layer)
+
+
+def test_w8a8_tiny_block_after_large_block():
+    """Every row: one block of amax 1e4 right before a block of amax 1e-30.  The running sums hold
+    S / c and move to the next block's scale by c_prev / c; without a floor on c that ratio
+    (about 1e34 here) overflows fp32.  The output must be finite and within tolerance."""
+    layer = _layer(BLOCKS.with_(name="w8a8_large_then_tiny", seed=46))
+    x = layer.x.float().cpu()
+    T, D = x.shape
+    nblk = D // 128
+    for t in range(T):
+        b = t % (nblk - 1)
+        big, tiny = slice(128 * b, 128 * (b + 1)), slice(128 * (b + 1), 128 * (b + 2))
+        x[t, big] *= 1e4 / x[t, big].abs().max()
+        x[t, tiny] *= 1e-30 / x[t, tiny].abs().max()
+    layer.x = x.to(torch.bfloat16).cuda()
     _check_h_codes(layer)
     _check(layer)
