@@ -43,6 +43,7 @@ struct PermArgs {
   int32_t *hist;        // [nblk][E]
   int32_t *units;       // [max units][4] chunk table (TM == 128), or nullptr
   int32_t *n_units;     // [1]
+  int id_bits;          // bits of the largest expert id (E - 1)
 };
 
 
@@ -97,6 +98,19 @@ __device__ void build_units(const PermArgs &a, const int *s_cnt_e, const int *s_
   if (threadIdx.x == 0) *a.n_units = s_u[kMaxE - 1];
 }
 
+// lanes of the wavefront holding the same expert id as this lane (e >= 0; lanes with e < 0
+// are in nobody's set): one ballot per bit of the id, so the cost is log2(E) ballots however
+// many distinct experts the 64 lanes hold
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, int id_bits) {
+  uint64_t same = __ballot(e >= 0);
+  for (int b = 0; b < id_bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  return same;
+}
+
 __device__ __forceinline__ int expert_of(const PermArgs &a, int64_t p) {
   if (p >= a.P) return -1;
   const int e = a.idx[p];
@@ -113,18 +127,8 @@ __device__ void count_block(const PermArgs &a, int blk, int (*s_cnt)[kMaxE]) {
   for (int c = 0; c < kPairsPerWave / 64; ++c) {
     const int64_t p = base + c * 64 + lane;
     const int e = expert_of(a, p);
-    uint64_t todo = __ballot(e >= 0);
-    int rank = 0, same = 0;
-    while (todo) {
-      const int leader = __ffsll(static_cast<long long>(todo)) - 1;
-      const int el = __builtin_amdgcn_readlane(e, leader);   // leader is wavefront-uniform
-      const uint64_t m = __ballot(e == el);
-      if (e == el) {
-        rank = __popcll(m & below);
-        same = __popcll(m);
-      }
-      todo &= ~m;
-    }
+    const uint64_t m = same_expert_lanes(e, a.id_bits);
+    const int rank = __popcll(m & below), same = __popcll(m);
     int r = 0;
     if (e >= 0) r = s_cnt[wave][e] + rank;
     __builtin_amdgcn_wave_barrier();
@@ -154,12 +158,20 @@ __device__ void count_block(const PermArgs &a, int blk, int (*s_cnt)[kMaxE]) {
 // phase 2, one workgroup of kPermThreads
 __device__ void scan_all(const PermArgs &a, int *s_pad, int *s_cnt_e, int *s_u) {
   for (int e = threadIdx.x; e < a.E; e += kPermThreads) {
+    // exclusive prefix over the count workgroups, eight histogram entries loaded at a time
+    // (one dependent load per entry left a global round trip per workgroup)
     int run = 0;
-    for (int b = 0; b < a.nblk; ++b) {
-      int32_t *h = a.hist + static_cast<int64_t>(b) * a.E + e;
-      const int v = *h;
-      *h = run;
-      run += v;
+    constexpr int kBatch = 8;
+    for (int b0 = 0; b0 < a.nblk; b0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        v[i] = b0 + i < a.nblk ? a.hist[static_cast<int64_t>(b0 + i) * a.E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (b0 + i < a.nblk) a.hist[static_cast<int64_t>(b0 + i) * a.E + e] = run;
+        run += v[i];
+      }
     }
     a.counts[e] = run;
     s_cnt_e[e] = run;
@@ -245,18 +257,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(PermArgs a)
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int e = ex[c];
-    uint64_t todo = __ballot(e >= 0);
-    int rank = 0, same = 0;
-    while (todo) {
-      const int leader = __ffsll(static_cast<long long>(todo)) - 1;
-      const int el = __builtin_amdgcn_readlane(e, leader);   // leader is wavefront-uniform
-      const uint64_t m = __ballot(e == el);
-      if (e == el) {
-        rank = __popcll(m & below);
-        same = __popcll(m);
-      }
-      todo &= ~m;
-    }
+    const uint64_t m = same_expert_lanes(e, a.id_bits);
+    const int rank = __popcll(m & below), same = __popcll(m);
     int r = 0;
     if (e >= 0) r = s_cnt[wave][e] + rank;
     __builtin_amdgcn_wave_barrier();
@@ -346,6 +348,8 @@ hipError_t launch_permute(const moe_config &cfg, int64_t T, const int32_t *topk_
   a.hist = r.scratch + a.P;
   a.units = nullptr;
   a.n_units = nullptr;
+  a.id_bits = 0;
+  while ((1 << a.id_bits) < a.E) ++a.id_bits;   // ids 0 .. E-1 fit in id_bits bits
   if (a.TM == 128) {
     int32_t *u = r.scratch + permute_units_offset(a.P, a.E);
     a.n_units = u;
