@@ -59,8 +59,8 @@ COUNTERS = {
                   "fetch_kib": 775590, "write_kib": 3424,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
-                "sha256": "b6d082a256501a24d4d3324f5f15a88789201da6147954e4fe05d7b45f527438",
-                "fetch_kib": 8314388, "write_kib": 194265,
+                "sha256": "5bcec851a917de6d314300c9c13dde315c3b8a60d8f64cc586eebcfc82fc69f4",
+                "fetch_kib": 8534842, "write_kib": 194706,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
     "v2_up": {"sources": ("gemm_expert.hip", "common.hpp"),
               "sha256": "ceea4922f60c05b526ebf70d1b7c9dffb6737db3104f090d1d9d89c21e123dac",
