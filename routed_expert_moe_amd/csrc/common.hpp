@@ -122,7 +122,7 @@ struct Plan {
 hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logits,
                              const float *bias, int32_t *topk_idx, float *topk_w, float *keys,
                              hipStream_t st);
-// logits[T, E] (fp32) = x[T, D] W_g^T on bf16 MFMA; supported: D a multiple of 64,
+// logits[T, E] (fp32) = x[T, D] W_g^T on bf16 MFMA; supported: D a multiple of 128,
 // x and W_g below 4 GiB each
 bool gate_logits_supported(int64_t T, int E, int D);
 hipError_t launch_gate_logits(int64_t T, int E, int D, const void *x, const void *w_gate, float *logits,

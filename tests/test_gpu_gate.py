@@ -4,7 +4,8 @@ moe_gate forms logits = x W_g^T (DeepSeek-V3 notes page, gate flow, step 1) on
 tiles of 64 tokens by 64 or 128 experts.  These shapes put the edges of that
 tiling under test: a ragged last row tile, a partly filled last column block,
 an expert count that is not a multiple of four (column-by-column stores), more
-than 256 experts, and a logits buffer that is only 4-byte aligned.  The
+than 256 experts, a logits buffer that is only 4-byte aligned, and a model
+width that is not a multiple of 128 (handled by the other GEMM).  The
 logits must match the oracle's to 1e-5 of their largest magnitude (fp32
 accumulation of exact bf16 products), and the selection must pass the
 certification protocol of tests/parity.py.
@@ -38,6 +39,8 @@ SHAPES = {
     "E256_T64_D7168": _shape("gate_E256_T64", T=64, D=7168, E=256, groups=8, keep=4, K=8),
     # 160 experts (three 64-wide blocks, the last of 32), 1000 tokens
     "E160_T1000": _shape("gate_E160_T1000", T=1000, D=1024, E=160, groups=1, keep=1, K=6, score="softmax"),
+    # a model width that is not a multiple of 128: the 128 x 128 register-staged tiles instead
+    "E64_D320_T100": _shape("gate_E64_D320", T=100, D=320, E=64, groups=4, keep=2, K=6),
 }
 
 
