@@ -467,7 +467,7 @@ def copy_probe(mib: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: every GPU box here has one, and no multi-GPU path is built; "
+        print(f"bench.py measures one GPU (the layer's single-GPU path; no multi-GPU path is built): "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import torch
