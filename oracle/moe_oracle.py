@@ -115,7 +115,9 @@ class Spec:
 # gate
 # --------------------------------------------------------------------------
 def sigmoid(z: np.ndarray) -> np.ndarray:
-    return 1.0 / (1.0 + np.exp(-z))
+    # for z < -709, exp(-z) overflows to inf and 1 / (1 + inf) = 0 is the correctly rounded value
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
 
 
 def gate_logits(x: np.ndarray, w_gate: np.ndarray) -> np.ndarray:
