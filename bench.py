@@ -372,7 +372,47 @@ def time_backward(p: Pass, shape, calls: int = 3):
            "ms_per_call": ms, "call_ms": stats(times), "tokens_per_s": T / (ms / 1e3), "gemm_flops": flops,
            "tflops": flops / (ms / 1e3) / 1e12, "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
            "workspace_bytes": ws.numel()}
-    del grads, ws
+
+    # The training variant: the forward's gate/up GEMM also keeps a and c in fp32
+    # (moe_expert_ffn_save) and the backward reads them instead of recomputing
+    # (moe_backward_saved): timed as that expert FFN against moe_expert_ffn, and the
+    # backward without its first GEMM (2 x gate/up + 2 x down + gate flops).
+    R = p.r.struct.max_rows
+    ab = torch.empty(R, 2 * I, dtype=torch.float32, device="cuda")
+    abs_ = torch.empty(T, 2 * S * I, dtype=torch.float32, device="cuda") if S else None
+
+    def ffn(save):
+        if save:
+            B.moe_expert_ffn_save(p.cfg, T, L.x, p.r, p.w, p.h, p.y, p.hs, p.z, ab, abs_)
+        else:
+            B.moe_expert_ffn(p.cfg, T, L.x, p.r, p.w, p.h, p.y, p.hs, p.z)
+
+    def saved():
+        B.moe_backward_saved(p.cfg, T, L.x, p.w, p.r, p.idx, p.tw, p.logits, p.y, dout, ab, abs_, grads,
+                             workspace=ws)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+    f_plain = timed(lambda: ffn(False), calls)
+    f_save = timed(lambda: ffn(True), calls)
+    b_saved = timed(saved, calls)
+    ms_s = sum(b_saved) / calls
+    flops_s = 2 * up + 2 * down + 4 * T * E * D
+    res["saved_preacts"] = {
+        "what": "moe_expert_ffn_save then moe_backward_saved (a and c kept by the forward in fp32)",
+        "expert_ffn_ms": sum(f_plain) / calls, "expert_ffn_save_ms": sum(f_save) / calls,
+        "backward_ms": ms_s, "backward_call_ms": stats(b_saved), "preact_bytes": (ab.numel() + (abs_.numel() if S else 0)) * 4,
+        "backward_tflops": flops_s / (ms_s / 1e3) / 1e12,
+        "training_step_ms_delta": (sum(f_save) - sum(f_plain)) / calls + ms_s - ms}
+    del grads, ws, ab, abs_
     torch.cuda.empty_cache()
     return res
 

@@ -193,6 +193,21 @@ moe_status moe_expert_ffn(const moe_config *cfg, int64_t T, const void *x,
                           const moe_routing *r, const moe_weights *w, void *h, void *y_pairs,
                           void *hs, void *z, void *stream);
 
+/* Training variant of moe_expert_ffn (notes page, SwiGLU experts; the layer
+ * backward below needs the SwiGLU's inputs a = W1_e x_t and c = W3_e x_t of every
+ * routed row and, with a shared expert, of every token).  Same arguments and
+ * outputs as moe_expert_ffn, bf16 activations and weights only
+ * (MOE_ERR_UNSUPPORTED otherwise), and it also writes:
+ *   ab  [max_rows, 2I] fp32: row i (routed-row order, as h) holds a in columns
+ *       [0, I) and c in [I, 2I), accumulated in fp32 exactly as the backward would
+ *       recompute them; padding rows hold unspecified values
+ *   abs [T, 2SI] fp32 when n_shared > 0 (hs and z are then required too): the shared
+ *       expert's a and c per token; ignored otherwise
+ * Both 16-byte aligned, caller-owned.  Pass them to moe_backward_saved. */
+moe_status moe_expert_ffn_save(const moe_config *cfg, int64_t T, const void *x, const moe_routing *r,
+                               const moe_weights *w, void *h, void *y_pairs, void *hs, void *z,
+                               float *ab, float *abs, void *stream);
+
 /* The two halves of moe_expert_ffn, for callers that schedule or time them
  * separately (same arguments and outputs as above):
  *   moe_expert_up:   h (and hs when hs != NULL) from x
@@ -326,6 +341,16 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
                         const float *logits, const void *y_pairs, const void *dout,
                         const moe_grads *grads, void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/* moe_backward without the recompute of a and c: ab / abs are what
+ * moe_expert_ffn_save wrote for this batch (abs only when n_shared > 0), read
+ * only.  Same arguments otherwise, same workspace size, and the same gradients
+ * bit for bit as moe_backward. */
+moe_status moe_backward_saved(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                              const moe_routing *r, const int32_t *topk_idx, const float *topk_w,
+                              const float *logits, const void *y_pairs, const void *dout,
+                              const float *ab, const float *abs, const moe_grads *grads,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -216,11 +216,15 @@ def silu(a: np.ndarray) -> np.ndarray:
     return a * sigmoid(a)
 
 
+def swiglu_preacts(xr: np.ndarray, w13: np.ndarray):
+    """The SwiGLU's two inputs for each row of xr: a = W1 u and c = W3 u, W13 = [W1; W3]."""
+    inter = w13.shape[0] // 2
+    return xr @ w13[:inter].T, xr @ w13[inter:].T
+
+
 def swiglu_ffn(xr: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
     """FFN(u) = W2 (silu(W1 u) * (W3 u)) for each row of xr; W13 = [W1; W3]."""
-    inter = w13.shape[0] // 2
-    a = xr @ w13[:inter].T
-    c = xr @ w13[inter:].T
+    a, c = swiglu_preacts(xr, w13)
     return (silu(a) * c) @ w2.T
 
 

@@ -68,7 +68,8 @@ EXPORTED = ("moe_validate", "moe_routing_size", "moe_routing_init", "moe_workspa
             "moe_status_str", "moe_last_error", "moe_gate", "moe_permute", "moe_expert_ffn",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_bias_update",
             "moe_quant_act", "moe_balance_loss", "moe_balance_loss_workspace_size",
-            "moe_backward", "moe_backward_workspace_size", "moe_forward_static")
+            "moe_backward", "moe_backward_workspace_size", "moe_forward_static",
+            "moe_expert_ffn_save", "moe_backward_saved")
 
 _lib = None
 
@@ -106,6 +107,10 @@ def lib():
         "moe_backward_workspace_size": [cfgp, I64, ctypes.POINTER(SZ)],
         "moe_backward": [cfgp, I64, P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing), P, P, P,
                          P, P, ctypes.POINTER(moe_grads), P, SZ, P],
+        "moe_expert_ffn_save": [cfgp, I64, P, ctypes.POINTER(moe_routing), ctypes.POINTER(moe_weights),
+                                P, P, P, P, P, P, P],
+        "moe_backward_saved": [cfgp, I64, P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing), P, P,
+                               P, P, P, P, P, ctypes.POINTER(moe_grads), P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -242,6 +247,15 @@ def moe_expert_ffn(cfg: moe_config, T: int, x, routing: Routing, weights: moe_we
                                 _stream(stream)))
 
 
+def moe_expert_ffn_save(cfg: moe_config, T: int, x, routing: Routing, weights: moe_weights, h, y_pairs,
+                        hs, z, ab, abs_, stream=None) -> None:
+    """moe_expert_ffn that also keeps the gate/up pre-activations: ab [max_rows, 2I] and
+    abs_ [T, 2SI] (None without a shared expert), fp32."""
+    _check(lib().moe_expert_ffn_save(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(routing.struct),
+                                     ctypes.byref(weights), _ptr(h), _ptr(y_pairs), _ptr(hs), _ptr(z),
+                                     _ptr(ab), _ptr(abs_), _stream(stream)))
+
+
 def moe_expert_up(cfg: moe_config, T: int, x, routing: Routing, weights: moe_weights, h, hs=None,
                   stream=None) -> None:
     _check(lib().moe_expert_up(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(routing.struct),
@@ -318,6 +332,18 @@ def moe_backward(cfg: moe_config, T: int, x, weights: moe_weights, routing: Rout
     _check(lib().moe_backward(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(weights), ctypes.byref(routing.struct),
                               _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(y_pairs), _ptr(dout),
                               ctypes.byref(g), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_backward_saved(cfg: moe_config, T: int, x, weights: moe_weights, routing: Routing, topk_idx, topk_w,
+                       logits, y_pairs, dout, ab, abs_, grads: Grads, workspace=None, stream=None) -> None:
+    """moe_backward reading the pre-activations moe_expert_ffn_save kept (ab, abs_)."""
+    if workspace is None:
+        workspace = _device_bytes(moe_backward_workspace_size(cfg, T), x)
+    g = grads.struct()
+    _check(lib().moe_backward_saved(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(weights),
+                                    ctypes.byref(routing.struct), _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
+                                    _ptr(y_pairs), _ptr(dout), _ptr(ab), _ptr(abs_), ctypes.byref(g),
+                                    _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def moe_bias_update(cfg: moe_config, T: int, routing: Routing, gamma: float, bias, stream=None) -> None:

@@ -259,9 +259,11 @@ moe_status do_gate(const moe_config &c, int64_t T, const void *x, const void *w_
 }
 
 // which: 1 = gate/up half, 2 = down half, 3 = both
+// ab / abs (optional): the gate/up pre-activations in fp32 ([rows, 2I] routed, [T, 2SI]
+// shared); only the prefill expert GEMM writes them, and *saved says whether it ran
 moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routing &r,
                   const moe_weights &w, void *h, void *y, void *hs, void *z, hipStream_t st,
-                  int which = 3) {
+                  int which = 3, float *ab = nullptr, float *abs = nullptr, bool *saved = nullptr) {
   const Plan p = plan_for(c, T);
   const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim;
   const bool fp8 = c.weight_dtype == MOE_FP8_E4M3_B128;
@@ -360,12 +362,22 @@ moe_status do_ffn(const moe_config &c, int64_t T, const void *x, const moe_routi
       dn[1].a_sld = SI / 128;
     }
   }
+  if (ab != nullptr) {
+    up[0].c_save = ab;
+    up[0].ld_save = 2 * I;
+    if (shared) {
+      up[1].c_save = abs;
+      up[1].ld_save = 2 * SI;
+    }
+  }
+  if (saved != nullptr) *saved = false;
   auto run = [&](Segment *segs, Epilogue epi) -> hipError_t {
     switch (p.path) {
       case PATH_F32: return launch_gemm_f32(segs, nseg, p.tile_m, epi, st);
       case PATH_FP8: return launch_gemm_fp8(segs, nseg, epi, st);
       case PATH_MFMA:
         if (r.tile_m == 128 && gemm_expert_supported(segs, nseg)) {
+          if (segs == up && saved != nullptr) *saved = true;
           const int32_t *nu = r.scratch + permute_units_offset(T * c.top_k, c.n_routed);
           const int64_t a_bytes = segs == up ? T * D * 2
                                              : std::max<int64_t>(static_cast<int64_t>(r.max_rows) * I, T * SI) * 2;
@@ -496,6 +508,45 @@ hipError_t store_gemm_f32(const Plan &p, Segment *segs, int nseg, hipStream_t st
   }
 }
 
+// a = W1_e x and c = W3_e x of every routed row ([rows, 2I] fp32: a then c) and, when
+// abs != nullptr, of the shared expert on every token ([T, 2SI]), as one fp32 GEMM
+hipError_t preact_gemm(const moe_config &c, int64_t T, const void *x, const moe_routing &r,
+                       const moe_weights &w, float *ab, float *abs, hipStream_t st) {
+  const Plan p = plan_for(c, T);
+  const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim;
+  Segment up[2] = {};
+  up[0].a = x;
+  up[0].lda = D;
+  up[0].gather = r.sorted_pair;
+  up[0].row_pair = r.sorted_pair;
+  up[0].topk = c.top_k;
+  up[0].b = w.w13;
+  up[0].b_stride = 2 * I * D;
+  up[0].n = static_cast<int32_t>(2 * I);
+  up[0].k = static_cast<int32_t>(D);
+  up[0].c = ab;
+  up[0].ldc = 2 * I;
+  up[0].tile_row = r.tile_row;
+  up[0].tile_expert = r.tile_expert;
+  up[0].expert_off = r.expert_off;
+  up[0].n_tiles_dev = r.n_tiles;
+  up[0].n_tiles_host = r.max_tiles;
+  int nseg = 1;
+  if (abs != nullptr && c.n_shared > 0) {
+    nseg = 2;
+    up[1].a = x;
+    up[1].lda = D;
+    up[1].a_rows = static_cast<int32_t>(T);
+    up[1].b = w.sw13;
+    up[1].n = static_cast<int32_t>(2 * SI);
+    up[1].k = static_cast<int32_t>(D);
+    up[1].c = abs;
+    up[1].ldc = 2 * SI;
+    up[1].n_tiles_host = static_cast<int32_t>((T + p.tile_m - 1) / p.tile_m);
+  }
+  return store_gemm_f32(p, up, nseg, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -605,6 +656,37 @@ moe_status moe_expert_ffn(const moe_config *cfg, int64_t T, const void *x,
   }
   if (T == 0) return ok();
   return do_ffn(*cfg, T, x, *r, *w, h, y_pairs, hs, z, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn_save(const moe_config *cfg, int64_t T, const void *x, const moe_routing *r,
+                               const moe_weights *w, void *h, void *y_pairs, void *hs, void *z, float *ab,
+                               float *abs, void *stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_bwd_cfg(*cfg));
+  MOE_NEED(x, "x");
+  MOE_TRY(check_routing(*cfg, T, r));
+  const bool shared = cfg->n_shared > 0;
+  MOE_TRY(check_weights(*cfg, w, shared));
+  MOE_NEED(h, "h");
+  MOE_NEED(y_pairs, "y_pairs");
+  if (ab == nullptr || !aligned16(ab)) return fail(MOE_ERR_INVALID_ARG, "ab must be non-NULL and 16-byte aligned");
+  if (shared) {
+    MOE_NEED(hs, "hs");
+    MOE_NEED(z, "z");
+    if (abs == nullptr || !aligned16(abs))
+      return fail(MOE_ERR_INVALID_ARG, "abs must be non-NULL and 16-byte aligned");
+  }
+  if (T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  bool saved = false;
+  MOE_TRY(do_ffn(*cfg, T, x, *r, *w, h, y_pairs, shared ? hs : nullptr, shared ? z : nullptr, st, 3, ab,
+                 shared ? abs : nullptr, &saved));
+  if (!saved) {   // a path whose gate/up GEMM keeps no fp32 copy: one more GEMM writes it
+    const hipError_t e = preact_gemm(*cfg, T, x, *r, *w, ab, shared ? abs : nullptr, st);
+    if (e != hipSuccess) return device_fail(e, "pre-activation GEMM launch");
+  }
+  return ok();
 }
 
 moe_status moe_expert_up(const moe_config *cfg, int64_t T, const void *x, const moe_routing *r,
@@ -772,10 +854,12 @@ moe_status moe_backward_workspace_size(const moe_config *cfg, int64_t T, size_t 
   return ok();
 }
 
-moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
-                        const moe_routing *r, const int32_t *topk_idx, const float *topk_w,
-                        const float *logits, const void *y_pairs, const void *dout, const moe_grads *g,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+// ab_in / abs_in: the pre-activations moe_expert_ffn_save kept, or nullptr to recompute them
+static moe_status backward_impl(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                                const moe_routing *r, const int32_t *topk_idx, const float *topk_w,
+                                const float *logits, const void *y_pairs, const void *dout,
+                                const float *ab_in, const float *abs_in, const moe_grads *g,
+                                void *workspace, size_t workspace_bytes, void *stream) {
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_T(*cfg, T));
   MOE_TRY(check_bwd_cfg(*cfg));
@@ -807,6 +891,8 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     if (!aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "x, weights, y_pairs, dout and the gradients must be 16-byte aligned");
   if (shared && (!aligned16(w->sw13) || !aligned16(w->sw2) || !aligned16(g->dsw13) || !aligned16(g->dsw2)))
     return fail(MOE_ERR_INVALID_ARG, "shared weights and gradients must be 16-byte aligned");
+  if (ab_in != nullptr && (!aligned16(ab_in) || (shared && !aligned16(abs_in))))
+    return fail(MOE_ERR_INVALID_ARG, "ab and abs must be non-NULL and 16-byte aligned");
   if (T == 0) return ok();
   const BwdLayout L = bwd_layout(c, T);
   if (workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
@@ -818,16 +904,17 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   hipStream_t st = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
-  const Plan p = plan_for(c, T);
-  const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim,
+    const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim,
                 E = c.n_routed, K = c.top_k;
   int32_t *trow = static_cast<int32_t *>(at(L.off_trow)), *texp = static_cast<int32_t *>(at(L.off_texp)),
           *tend = static_cast<int32_t *>(at(L.off_tend)), *tfirst = static_cast<int32_t *>(at(L.off_tfirst)),
           *nt = static_cast<int32_t *>(at(L.off_nt));
-  float *ab = static_cast<float *>(at(L.off_ab)), *dh = static_cast<float *>(at(L.off_dh)),
+  const float *ab = ab_in != nullptr ? ab_in : static_cast<float *>(at(L.off_ab));
+  float *dh = static_cast<float *>(at(L.off_dh)),
         *dxp = static_cast<float *>(at(L.off_dxp)), *dw = static_cast<float *>(at(L.off_dw)),
-        *dxg = static_cast<float *>(at(L.off_dxg)), *abs_ = static_cast<float *>(at(L.off_abs)),
-        *dhs = static_cast<float *>(at(L.off_dhs)), *dxs = static_cast<float *>(at(L.off_dxs));
+        *dxg = static_cast<float *>(at(L.off_dxg)), *dhs = static_cast<float *>(at(L.off_dhs)),
+        *dxs = static_cast<float *>(at(L.off_dxs));
+  const float *abs_ = ab_in != nullptr ? abs_in : static_cast<float *>(at(L.off_abs));
   void *dy = at(L.off_dy), *hb = at(L.off_h), *dab = at(L.off_dab), *dl = at(L.off_dl), *hsb = at(L.off_hsb),
        *dabs = at(L.off_dabs), *xs = at(L.off_xs);
   auto bf = [](const void *q) { return static_cast<const uint16_t *>(q); };
@@ -838,38 +925,11 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     if (e != hipSuccess) return device_fail(e, what); \
   } while (0)
 
-  // 1. a, c of every used row again (the forward kept only h): [rows, 2I] fp32
-  Segment up[2] = {};
-  up[0].a = x;
-  up[0].lda = D;
-  up[0].gather = r->sorted_pair;
-  up[0].row_pair = r->sorted_pair;
-  up[0].topk = c.top_k;
-  up[0].b = w->w13;
-  up[0].b_stride = 2 * I * D;
-  up[0].n = static_cast<int32_t>(2 * I);
-  up[0].k = static_cast<int32_t>(D);
-  up[0].c = ab;
-  up[0].ldc = 2 * I;
-  up[0].tile_row = r->tile_row;
-  up[0].tile_expert = r->tile_expert;
-  up[0].expert_off = r->expert_off;
-  up[0].n_tiles_dev = r->n_tiles;
-  up[0].n_tiles_host = r->max_tiles;
-  int nseg = 1;
-  if (shared) {
-    nseg = 2;
-    up[1].a = x;
-    up[1].lda = D;
-    up[1].a_rows = static_cast<int32_t>(T);
-    up[1].b = w->sw13;
-    up[1].n = static_cast<int32_t>(2 * SI);
-    up[1].k = static_cast<int32_t>(D);
-    up[1].c = abs_;
-    up[1].ldc = 2 * SI;
-    up[1].n_tiles_host = static_cast<int32_t>((T + p.tile_m - 1) / p.tile_m);
-  }
-  MOE_BWD(store_gemm_f32(p, up, nseg, st), "backward gate/up recompute launch");
+  // 1. a, c of every used row again, unless the forward kept them: [rows, 2I] fp32
+  if (ab_in == nullptr)
+    MOE_BWD(preact_gemm(c, T, x, *r, *w, static_cast<float *>(at(L.off_ab)),
+                        shared ? static_cast<float *>(at(L.off_abs)) : nullptr, st),
+            "backward gate/up recompute launch");
   MOE_BWD(launch_bwd_tiles(r->expert_off, c.n_routed, trow, texp, tend, tfirst, nt, st),
           "backward tile list launch");
 
@@ -896,7 +956,8 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
   q.n = static_cast<int32_t>(I);
   q.k = static_cast<int32_t>(D);
   MOE_BWD(rows_gemm(q, r, st), "backward dh launch");
-  MOE_BWD(launch_swiglu_bwd(ab, dh, r->n_tiles, r->tile_m, r->max_rows, static_cast<int>(I), hb, dab, st),
+  MOE_BWD(launch_swiglu_bwd(ab, dh, r->n_tiles, r->tile_m, r->max_rows, static_cast<int>(I), r->sorted_pair,
+                            hb, dab, st),
           "backward SwiGLU launch");
   q = rg;
   q.a = bf(dab);
@@ -952,7 +1013,7 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
     q.n = static_cast<int32_t>(SI);
     q.k = static_cast<int32_t>(D);
     MOE_BWD(rows_gemm(q, nullptr, st), "backward shared dh launch");
-    MOE_BWD(launch_swiglu_bwd(abs_, dhs, nullptr, 0, T, static_cast<int>(SI), hsb, dabs, st),
+    MOE_BWD(launch_swiglu_bwd(abs_, dhs, nullptr, 0, T, static_cast<int>(SI), nullptr, hsb, dabs, st),
             "backward shared SwiGLU launch");
     q = dg;
     q.a = bf(dabs);
@@ -1024,6 +1085,25 @@ moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const m
           "backward dx launch");
 #undef MOE_BWD
   return ok();
+}
+
+moe_status moe_backward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                        const moe_routing *r, const int32_t *topk_idx, const float *topk_w,
+                        const float *logits, const void *y_pairs, const void *dout, const moe_grads *g,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  return backward_impl(cfg, T, x, w, r, topk_idx, topk_w, logits, y_pairs, dout, nullptr, nullptr, g,
+                       workspace, workspace_bytes, stream);
+}
+
+moe_status moe_backward_saved(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                              const moe_routing *r, const int32_t *topk_idx, const float *topk_w,
+                              const float *logits, const void *y_pairs, const void *dout,
+                              const float *ab, const float *abs, const moe_grads *g, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  if (ab == nullptr) return fail(MOE_ERR_INVALID_ARG, "ab is NULL");
+  if (cfg != nullptr && cfg->n_shared > 0 && abs == nullptr) return fail(MOE_ERR_INVALID_ARG, "abs is NULL");
+  return backward_impl(cfg, T, x, w, r, topk_idx, topk_w, logits, y_pairs, dout, ab, abs, g, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

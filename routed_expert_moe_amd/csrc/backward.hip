@@ -113,13 +113,20 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 // rows [0, rows) (rows_dev: n_tiles * tile_m when given), I columns
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
     const float *__restrict__ ab, const float *__restrict__ dh, const int32_t *__restrict__ n_tiles,
-    int tile_m, int64_t rows_host, int I, uint16_t *__restrict__ h, uint16_t *__restrict__ dab) {
+    int tile_m, int64_t rows_host, int I, const int32_t *__restrict__ row_pair,
+    uint16_t *__restrict__ h, uint16_t *__restrict__ dab) {
   const int64_t rows = n_tiles ? static_cast<int64_t>(*n_tiles) * tile_m : rows_host;
   const int64_t n = rows * I;
   for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < n;
        q += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t r = q / I;
     const int i = static_cast<int>(q - r * I);
+    if (row_pair != nullptr && row_pair[r] < 0) {   // a padding row: its a and c may be unset
+      h[r * I + i] = 0;
+      dab[r * 2 * I + i] = 0;
+      dab[r * 2 * I + I + i] = 0;
+      continue;
+    }
     const float a = ab[r * 2 * I + i], c = ab[r * 2 * I + I + i], d = dh[r * I + i];
     const float sa = 1.0f / (1.0f + expf(-a));
     h[r * I + i] = f32_to_bf16_bits(a * sa * c);
@@ -258,13 +265,15 @@ hipError_t launch_combine_bwd(const void *dout, const void *y, const moe_routing
 }
 
 hipError_t launch_swiglu_bwd(const float *ab, const float *dh, const int32_t *n_tiles, int tile_m,
-                             int64_t rows_host, int I, void *h, void *dab, hipStream_t st) {
+                             int64_t rows_host, int I, const int32_t *row_pair, void *h, void *dab,
+                             hipStream_t st) {
   const int64_t n = rows_host * I;
   if (n == 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, ab, dh,
-                     n_tiles, tile_m, rows_host, I, static_cast<uint16_t *>(h), static_cast<uint16_t *>(dab));
+                     n_tiles, tile_m, rows_host, I, row_pair, static_cast<uint16_t *>(h),
+                     static_cast<uint16_t *>(dab));
   return hipGetLastError();
 }
 

@@ -34,8 +34,11 @@ hipError_t launch_combine_bwd(const void *dout, const void *y, const moe_routing
                               int K, int D, void *dy, float *dw, hipStream_t st);
 // xs[r] = x[sorted_pair[r] / K] for every used routed row (zeros for padding)
 hipError_t launch_gather_rows(const void *x, const moe_routing &r, int K, int D, void *xs, hipStream_t st);
+// h = silu(a) c, da = dh c silu'(a), dc = dh silu(a) per row of ab = [a | c]; rows whose
+// row_pair entry is negative (padding) get zeros whatever ab holds
 hipError_t launch_swiglu_bwd(const float *ab, const float *dh, const int32_t *n_tiles, int tile_m,
-                             int64_t rows_host, int I, void *h, void *dab, hipStream_t st);
+                             int64_t rows_host, int I, const int32_t *row_pair, void *h, void *dab,
+                             hipStream_t st);
 hipError_t launch_gate_bwd(const moe_config &cfg, int64_t T, const float *logits, const int32_t *topk_idx,
                            const int32_t *pair_row, const float *dw, void *dl, hipStream_t st);
 hipError_t launch_dx_final(int64_t T, int K, int D, int residual, const void *dout, const float *dx_shared,

@@ -95,6 +95,10 @@ struct Segment {
   int32_t n_tiles_host;        // dense tile count, or capacity for routed
   const int32_t *row_pair;     // routed rows' sorted_pair (< 0 marks padding), or nullptr
   int64_t ldb;                 // k-strided B (backward row form): elements per B row
+  // SwiGLU epilogue of the prefill expert GEMM: when set, the pre-activations a
+  // (columns [0, n/2)) and c (columns [n/2, n)) of every real row also go out in fp32
+  float *c_save;
+  int64_t ld_save;             // floats between rows of c_save
 };
 
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1 };

@@ -45,6 +45,9 @@
 // Epilogue: SwiGLU (silu(gate) * up in fp32) or plain; the bf16 tile is staged
 // in LDS and written as whole row runs.  Only rows that hold a real pair
 // (routed) or a token (dense) are written; padding rows keep unspecified values.
+// A training forward can also keep the SwiGLU's inputs: with c_save set, each
+// real row's gate and up pre-activations are stored in fp32 straight from the
+// accumulators (16 bytes per lane), so the backward need not recompute them.
 #include "common.hpp"
 #include <type_traits>
 
@@ -130,6 +133,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_expert_kernel(ExpertWork wk)
     const int K = uniform(SEGF(k));
     void *c_base = uptr(SEGF(c));
     const int64_t ldc = SEGF(ldc);
+    float *c_save = uptr(SEGF(c_save));
+    const int64_t ld_save = SEGF(ld_save);
 #undef SEGF
     const int local = s1 ? w - items0 : w;
     const int nb1 = s1 ? wk.nb1[1] : wk.nb1[0];
@@ -360,6 +365,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_expert_kernel(ExpertWork wk)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int lc = n_grp * 32 + 8 * g + 4 * khalf;
+            if (c_save != nullptr && row0 + lr < real_end && nb * OUT + lc < ncols) {
+              // the pre-activations a and c of this row's four columns, in fp32
+              float *dst = c_save + static_cast<int64_t>(row0 + lr) * ld_save + nb * OUT + lc;
+              const f32x4_t av = {acc[i][0][4 * g], acc[i][0][4 * g + 1], acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]};
+              const f32x4_t cv = {acc[i][1][4 * g], acc[i][1][4 * g + 1], acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]};
+              __builtin_nontemporal_store(av, reinterpret_cast<f32x4_t *>(dst));
+              __builtin_nontemporal_store(cv, reinterpret_cast<f32x4_t *>(dst + half_n));
+            }
             float h[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) h[t] = silu_mul(acc[i][0][4 * g + t], acc[i][1][4 * g + t]);

@@ -214,6 +214,38 @@ def test_backward_validates_before_launch():
     assert B.moe_backward_workspace_size(c, 2 * T) > need
 
 
+def test_saved_preactivation_entry_points_validate_before_launch():
+    L = B.lib()
+    fake = 1 << 20
+    c = B.config_of(configs.V2_LITE_BF16)   # two shared experts
+    T = 64
+    need = B.moe_backward_workspace_size(c, T)
+    r = B.moe_routing_init(c, T, fake, B.moe_routing_size(c, T))
+    w = B.moe_weights(w_gate=fake, w13=fake, w2=fake, sw13=fake, sw2=fake)
+    g = B.moe_grads(dx=fake, dw_gate=fake, dw13=fake, dw2=fake, dsw13=fake, dsw2=fake)
+    ws = 1 << 32
+
+    def ffn(cfg=c, T=T, ab=fake, abs_=fake, hs=fake):
+        return L.moe_expert_ffn_save(ctypes.byref(cfg), T, fake, ctypes.byref(r), ctypes.byref(w), fake, fake,
+                                     hs, fake, ab, abs_, None)
+
+    def bwd(ab=fake, abs_=fake, nb=need):
+        return L.moe_backward_saved(ctypes.byref(c), T, fake, ctypes.byref(w), ctypes.byref(r), fake, fake,
+                                    fake, fake, fake, ab, abs_, ctypes.byref(g), ws, nb, None)
+    assert ffn(ab=None) == B.MOE_ERR_INVALID_ARG
+    assert ffn(ab=fake + 4) == B.MOE_ERR_INVALID_ARG                # 16-byte alignment
+    assert ffn(abs_=None) == B.MOE_ERR_INVALID_ARG                  # a shared expert needs abs
+    assert ffn(hs=None) == B.MOE_ERR_INVALID_ARG
+    assert ffn(cfg=B.config_of(configs.V3_DECODE_FP8), T=8) == B.MOE_ERR_UNSUPPORTED   # bf16 only
+    assert bwd(ab=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(abs_=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(abs_=fake + 8) == B.MOE_ERR_INVALID_ARG
+    assert bwd(nb=need - 1) == B.MOE_ERR_WORKSPACE
+    r0 = B.moe_routing_init(c, 0, fake, B.moe_routing_size(c, 0))
+    assert L.moe_expert_ffn_save(ctypes.byref(c), 0, fake, ctypes.byref(r0), ctypes.byref(w), fake, fake,
+                                 fake, fake, fake, fake, None) == B.MOE_OK
+
+
 def test_static_forward_rejects_layers_beyond_its_scratch():
     """moe_forward_static checks its workspace need against the static array on the
     host, before any device call: the V3 prefill batch needs far more than 64 MiB."""

@@ -250,6 +250,20 @@ def test_swiglu_closed_form_permutations():
     assert np.allclose(got, want, rtol=0, atol=1e-15)
 
 
+def test_swiglu_preacts_unit_inputs_pick_columns():
+    """u = e_j gives a = column j of W1 and c = column j of W3 (W13 = [W1; W3], rows
+    first the gate half); a sum of two unit inputs gives the sum of the columns."""
+    rng = np.random.default_rng(11)
+    D, I = 7, 4
+    w13 = rng.normal(size=(2 * I, D))
+    for j in range(D):
+        a, c = oracle.swiglu_preacts(np.eye(D)[j:j + 1], w13)
+        assert np.array_equal(a[0], w13[:I, j]) and np.array_equal(c[0], w13[I:, j])
+    a, c = oracle.swiglu_preacts((np.eye(D)[1] + np.eye(D)[5])[None], w13)
+    assert np.allclose(a[0], w13[:I, 1] + w13[:I, 5], rtol=0, atol=1e-15)
+    assert np.allclose(c[0], w13[I:, 1] + w13[I:, 5], rtol=0, atol=1e-15)
+
+
 def test_swiglu_brute_force_loops():
     rng = np.random.default_rng(4)
     D, I = 5, 3
