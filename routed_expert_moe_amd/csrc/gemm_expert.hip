@@ -279,9 +279,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_expert_kernel(ExpertWork wk)
             bf[j] = __builtin_bit_cast(bf16x8_t, brows[r * 8 + (c ^ swz(r))]);
           }
         };
-        // the loads of the steps after kt, issued right after step kt's barrier: the
-        // stages they fill were last read in step kt-1
-        auto issue_next = [&](int kt) __attribute__((always_inline)) {
+        // the loads of the steps after kt, issued after step kt's barrier: the stages they
+        // fill were last read in step kt-1.  They go out a quarter per K-slice (issue_part
+        // q = 0..3, A loads first, then B, as in issue_next, so the waits count the same
+        // loads): eight 1 KiB loads per wavefront at once kept the texture unit's address
+        // and command FIFOs full on 12-15% of the cycles, stalling the MFMAs queued behind
+        // the loads; spread out, the prefill gate/up launch takes ~2% less time.
+        auto issue_part = [&](int kt, auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value, L = NA + NB_L;
+          constexpr int lo = q * L / 4, hi = (q + 1) * L / 4;
+          const bool a_ok = kt + 1 < nk, b_ok = kB3 ? kt + 2 < nk : kt + 1 < nk;
+          const int kb = kB3 ? kt + 2 : kt + 1;
+#pragma unroll
+          for (int i = lo; i < hi; ++i) {
+            if (i < NA) {
+              if (a_ok) load_lds16(ra, voff[i], static_cast<uint32_t>((kt + 1) * BK * 2), a_st(kt + 1) + lrow_of[i] * kRowBytes);
+            } else {
+              if (b_ok) load_lds16(rb, voff[i], static_cast<uint32_t>(kb * BK * 2), b_st(kb) + lrow_of[i] * kRowBytes);
+            }
+          }
+        };
+        auto issue_next = [&](int kt) __attribute__((always_inline)) {   // all at once
           if (kB3) {
             if (kt + 1 < nk) issue_a(kt + 1);
             if (kt + 2 < nk) issue_b(kt + 2);
@@ -318,7 +336,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_expert_kernel(ExpertWork wk)
             read_frags(sa, sb, 0, af[0], bf[0]);
 #pragma unroll
             for (int s = 0; s < BK / 16; ++s) {
-              if (s == 0) issue_next(kt);
+              if (s == 0) issue_part(kt, std::integral_constant<int, 0>{});
+              if (s == 1) issue_part(kt, std::integral_constant<int, 1>{});
+              if (s == 2) issue_part(kt, std::integral_constant<int, 2>{});
+              if (s == 3) issue_part(kt, std::integral_constant<int, 3>{});
               if (s + 1 < BK / 16) read_frags(sa, sb, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
 #pragma unroll
               for (int i = 0; i < NB; ++i)
