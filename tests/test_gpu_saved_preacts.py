@@ -10,7 +10,8 @@ feed silu(a) * c to W2_e; the layer backward needs a and c again.  Checked here:
   * moe_backward_saved gives the same gradients as moe_backward bit for bit, on the
     backward test shapes (the 16-row streaming path, where the save falls back to one
     more fp32 GEMM, and the 128-row prefill path, where the expert GEMM writes a and c
-    from its accumulators), V2-Lite and the V3 prefill batch at full size."""
+    from its accumulators), a 128-row shape whose K rules out the prefill expert GEMM
+    (the fallback again), V2-Lite and the V3 prefill batch at full size."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +21,7 @@ from oracle_bridge import expert_fn, shared_pair, to_f64
 from parity import say
 from routed_expert_moe_amd import binding as B
 from routed_expert_moe_amd import configs, synth
+from routed_expert_moe_amd.configs import LayerShape
 from test_gpu_backward import SHAPES as BWD_SHAPES
 
 pytestmark = pytest.mark.gpu
@@ -134,6 +136,11 @@ def _same_grads(g1, g2, shared):
 
 CASES = dict(BWD_SHAPES)
 CASES["v2lite_bf16_T512"] = configs.V2_LITE_BF16
+# dim 352 (not a multiple of 64): the 128-row MFMA path without the prefill expert GEMM,
+# so the save falls back to the separate fp32 GEMM there too
+CASES["mfma_dim352"] = LayerShape(
+    name="save_d352", T=512, dim=352, n_routed=16, n_groups=4, topk_groups=2, top_k=4, n_shared=1,
+    inter_dim=128, score="sigmoid", route_scale=2.5, act="bf16", weight="bf16", seed=38, bias_range=0.1)
 
 
 @pytest.mark.parametrize("name", list(CASES))
