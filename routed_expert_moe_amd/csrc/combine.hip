@@ -1,8 +1,10 @@
 // Combine (DeepSeek-V3 notes page, "DeepSeekMoE" total-output equation):
 //   out[t] = u[t] + z[t] + sum_k w[t,k] * y[pair_row[t*K+k]]
-// grid.x is the token, grid.y splits the row; every thread owns 16-byte column chunks and sums in
-// fp32 in a fixed order (u, z, then slots k = 0..K-1, which the gate emits in
-// ascending expert order), rounding once.  No atomics: the result is unique.
+// grid.x is the token, grid.y splits the row; every thread owns 16-byte column chunks, two
+// at a time with all their loads issued before the first sum (the kernel is bound by the
+// loads it keeps in flight), and sums each in fp32 in a fixed order (u, z, then slots
+// k = 0..K-1, which the gate emits in ascending expert order), rounding once.  No
+// atomics: the result is unique.
 #include "common.hpp"
 
 namespace moe {
@@ -30,53 +32,77 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int
   __syncthreads();
   constexpr int V = BF16 ? 8 : 4;   // elements per 16-byte chunk
   const int nchunks = D / V;
-  for (int c = blockIdx.y * kThreads + threadIdx.x; c < nchunks; c += kThreads * gridDim.y) {
-    float acc[V];
+  constexpr int CH = 2;   // chunks per thread and iteration
+  const int stride = kThreads * gridDim.y;
+  for (int c0 = blockIdx.y * kThreads + threadIdx.x; c0 < nchunks; c0 += CH * stride) {
+    int cc[CH];
+    bool ok[CH];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-    auto load = [&](const void *base, int64_t row) -> u32x4_t {
-      return reinterpret_cast<const u32x4_t *>(base)[(row * D) / V + c];
+    for (int q = 0; q < CH; ++q) {
+      cc[q] = c0 + q * stride;
+      ok[q] = cc[q] < nchunks;
+      if (!ok[q]) cc[q] = c0;            // a chunk past the row loads a valid one, unused
+    }
+    float acc[CH][V];
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[q][i] = 0.0f;
+    auto load = [&](const void *base, int64_t row, int q) -> u32x4_t {
+      return reinterpret_cast<const u32x4_t *>(base)[(row * D) / V + cc[q]];
     };
-    auto add_row = [&](const u32x4_t v, float scale, bool fma_mode) {
+    auto add_row = [&](int q, const u32x4_t v, float scale, bool fma_mode) {
       if (BF16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
-          acc[2 * i] = fma_mode ? fmaf(scale, lo, acc[2 * i]) : acc[2 * i] + lo;
-          acc[2 * i + 1] = fma_mode ? fmaf(scale, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+          acc[q][2 * i] = fma_mode ? fmaf(scale, lo, acc[q][2 * i]) : acc[q][2 * i] + lo;
+          acc[q][2 * i + 1] = fma_mode ? fmaf(scale, hi, acc[q][2 * i + 1]) : acc[q][2 * i + 1] + hi;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float f = __uint_as_float(v[i]);
-          acc[i] = fma_mode ? fmaf(scale, f, acc[i]) : acc[i] + f;
+          acc[q][i] = fma_mode ? fmaf(scale, f, acc[q][i]) : acc[q][i] + f;
         }
       }
     };
-    // loads are issued in batches before their first use; an absent term (no
-    // residual, no shared expert, a dropped slot with row -1) reads row 0 of y,
-    // which always exists, and is skipped when summing
-    const u32x4_t vu = residual ? load(u, t) : load(y, 0);
-    const u32x4_t vz = z != nullptr ? load(z, t) : load(y, 0);
-    if (residual) add_row(vu, 1.0f, false);
-    if (z != nullptr) add_row(vz, 1.0f, false);
+    u32x4_t vu[CH], vz[CH];
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      vu[q] = residual ? load(u, t, q) : load(y, 0, q);
+      vz[q] = z != nullptr ? load(z, t, q) : load(y, 0, q);
+    }
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      if (residual) add_row(q, vu[q], 1.0f, false);
+      if (z != nullptr) add_row(q, vz[q], 1.0f, false);
+    }
     for (int k0 = 0; k0 < K; k0 += kBatch) {
-      u32x4_t v[kBatch];
+      u32x4_t v[CH][kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) v[i] = load(y, max(s_row[min(k0 + i, K - 1)], 0));
+      for (int q = 0; q < CH; ++q)
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (k0 + i < K && s_row[k0 + i] >= 0) add_row(v[i], s_w[k0 + i], true);
+        for (int i = 0; i < kBatch; ++i) v[q][i] = load(y, max(s_row[min(k0 + i, K - 1)], 0), q);
+#pragma unroll
+      for (int q = 0; q < CH; ++q)
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (k0 + i < K && s_row[k0 + i] >= 0) add_row(q, v[q][i], s_w[k0 + i], true);
     }
-    u32x4_t o;
-    if (BF16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    } else {
+    for (int q = 0; q < CH; ++q) {
+      if (!ok[q]) continue;
+      u32x4_t o;
+      if (BF16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[q][2 * i], acc[q][2 * i + 1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[q][i]);
+      }
+      reinterpret_cast<u32x4_t *>(out)[(t * D) / V + cc[q]] = o;
     }
-    reinterpret_cast<u32x4_t *>(out)[(t * D) / V + c] = o;
   }
 }
 
