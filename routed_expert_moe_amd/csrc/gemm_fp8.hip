@@ -18,6 +18,13 @@
 // block's MFMAs, and the epilogue multiplies by the last c.  That is exact up to
 // one fp32 rounding per block.
 //
+// The next step's ten 1 KiB tile loads per wavefront go out in four parts, before and
+// in the middle of each K-slice's MFMAs: issued at once after the barrier they kept the
+// texture unit's address and command FIFOs full on 27-31% of the cycles and the MFMAs
+// behind them waiting (gate/up 3.78 -> 3.2-3.3 ms at V3 prefill).  The last step loads
+// block nk-1 once more into the free stage instead of branching around the loads, which
+// would split the slice's code.
+//
 // Routed tiles skip the MFMAs, fragment reads and rescaling of 32-row blocks
 // that hold only padding (an expert's last tile); those rows come out as zeros.
 //
@@ -174,6 +181,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
       const int r = (wave * kBLoads + i) * 8 + lrow;
       boff[i] = static_cast<uint32_t>(b_row(r)) * static_cast<uint32_t>(K) + (pch ^ swz(r)) * 16;
     }
+    // part q (of 4) of the kLoads tile loads of step kt into `stage`: A loads first, then B;
+    // every wavefront waits for all of them at the next step, so the order needs no care
+    auto issue_part = [&](int kt, int stage, int q) {
+      char *st = lds + stage * kStageBytes;
+      const uint32_t k0 = static_cast<uint32_t>(kt * BK);
+#pragma unroll
+      for (int l = 0; l < kLoads; ++l) {
+        if (l < q * kLoads / 4 || l >= (q + 1) * kLoads / 4) continue;
+        if (l < kALoads) load_lds16(ra, aoff[l], k0, st + (wave * kALoads + l) * 1024);
+        else load_lds16(rb, boff[l - kALoads], k0, st + kATileBytes + (wave * kBLoads + l - kALoads) * 1024);
+      }
+    };
     auto issue = [&](int kt) {
       char *st = lds + (kt & 1) * kStageBytes;
       const uint32_t k0 = static_cast<uint32_t>(kt * BK);
@@ -249,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
     auto kloop = [&](auto nbc) {
       constexpr int NB = decltype(nbc)::value;
       // block 0's scales seed c_prev (the first rescale multiplies zeros by one); the
-      // last step issues no loads (its scale reads fetch block nk-1 again, harmlessly)
+      // last step's loads fetch block nk-1 again, unused (its tiles into the free stage)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sa[i] = sa_max[i] = ascale(i, 0);
 #pragma unroll
@@ -269,7 +288,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
         float sa_next[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sa_next[i] = ascale(i, kn);
-        if (kt + 1 < nk) issue(kn);   // the other stage: every wavefront finished reading it
+        // the other stage: every wavefront finished reading it (the last step loads block
+        // nk-1 there once more, unused, so that no branch splits the slice's code)
         // rescale the running sums from block kt-1's scale to block kt's
         float sae[4];
 #pragma unroll
@@ -300,6 +320,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
           for (int j = 0; j < NJ; ++j) bf[j] = read_frag(st + kATileBytes, brow_l[j], s);
 #pragma unroll
           for (int i = 0; i < NB; ++i) {
+            if (i == 0) issue_part(kn, (kt + 1) & 1, 2 * s);
+            if (i == (NB > 1 ? (NB + 1) / 2 : 0)) issue_part(kn, (kt + 1) & 1, 2 * s + 1);
             const v8i_t af = read_frag(st, i * 32 + l32, s);
 #pragma unroll
             for (int j = 0; j < NJ; ++j)   // weight fragment first: lanes end with 4 consecutive columns
@@ -319,7 +341,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(WorkF8 wk) {
       case 3: kloop(std::integral_constant<int, 3>{}); break;
       default: kloop(std::integral_constant<int, 4>{}); break;
     }
-    // every load has landed (the last step issued none) and all waves are done with both stages
+    // every load has landed (the last step's into the free stage too) and all waves are done
+    // with both stages
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
 
