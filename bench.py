@@ -51,24 +51,24 @@ PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector)
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-                   "sha256": "cbc4743ab21c05bd1ac932af7f70520f638929f9b1d720d055f5168a1e1e8988",
-                   "fetch_kib": 12200906, "write_kib": 294912,
+                   "sha256": "e82bd00bd8bd5b049c85eb060cfa49809888942fe324a4c4dd5e9678cc105e47",
+                   "fetch_kib": 12199832, "write_kib": 294912,
                    "profile": "profiles/gemm_expert_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
                   "sha256": "8a86871ecd0fe49301b9a4f87bb3f4bf23a9523c288db51e2882de059ffe939c",
-                  "fetch_kib": 775591, "write_kib": 3424,
+                  "fetch_kib": 775595, "write_kib": 3424,
                   "profile": "profiles/gemm_skinny_gate_up_v3_decode_T8_counters.md"},
     "w8a8_up": {"sources": ("gemm_fp8.hip", "common.hpp"),
-                "sha256": "1eec33008e67dd3ada6b07c2cc7a79c6917f9a09d8aab89db4c92769df295dcb",
-                "fetch_kib": 8551990, "write_kib": 194523,
+                "sha256": "63849d515b9b3c98d3dfc500ddc0df40c5f38181b6a4d9f3e9df9ae0b3fc1e66",
+                "fetch_kib": 5046430, "write_kib": 190350,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
     "v2_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-              "sha256": "cbc4743ab21c05bd1ac932af7f70520f638929f9b1d720d055f5168a1e1e8988",
-              "fetch_kib": 3103051, "write_kib": 98304,
+              "sha256": "e82bd00bd8bd5b049c85eb060cfa49809888942fe324a4c4dd5e9678cc105e47",
+              "fetch_kib": 3110751, "write_kib": 98304,
               "profile": "profiles/gemm_expert_gate_up_v2_T4096_counters.md"},
     "ep_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-              "sha256": "cbc4743ab21c05bd1ac932af7f70520f638929f9b1d720d055f5168a1e1e8988",
-              "fetch_kib": 1282900, "write_kib": 32768,
+              "sha256": "e82bd00bd8bd5b049c85eb060cfa49809888942fe324a4c4dd5e9678cc105e47",
+              "fetch_kib": 1283557, "write_kib": 32768,
               "profile": "profiles/gemm_expert_gate_up_v3_ep_shard_T4096_E32_counters.md"},
 }
 
