@@ -904,7 +904,7 @@ static moe_status backward_impl(const moe_config *cfg, int64_t T, const void *x,
   hipStream_t st = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
-    const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim,
+  const int64_t D = c.dim, I = c.inter_dim, SI = static_cast<int64_t>(c.n_shared) * c.inter_dim,
                 E = c.n_routed, K = c.top_k;
   int32_t *trow = static_cast<int32_t *>(at(L.off_trow)), *texp = static_cast<int32_t *>(at(L.off_texp)),
           *tend = static_cast<int32_t *>(at(L.off_tend)), *tfirst = static_cast<int32_t *>(at(L.off_tfirst)),
