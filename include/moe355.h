@@ -176,7 +176,9 @@ moe_status moe_gate(const moe_config *cfg, int64_t T, const void *x, const void 
 moe_status moe_permute(const moe_config *cfg, int64_t T, const int32_t *topk_idx,
                        const moe_routing *r, void *stream);
 
-/* Expert FFNs: for every used row i of expert e holding pair p = t*K + k,
+/* Expert FFNs (notes page, "DeepSeekMoE" paragraph: the routed experts FFN_r and
+ * the shared experts FFN_share, each a SwiGLU FFN): for every used row i of
+ * expert e holding pair p = t*K + k,
  *   h[i]       = silu(W1_e x_t) * (W3_e x_t)               [max_rows, I] act dtype
  *   y_pairs[i] = W2_e h[i]                                   [max_rows, D] act dtype
  * and, when z != NULL, the shared expert on every token:
@@ -208,7 +210,8 @@ moe_status moe_expert_ffn_save(const moe_config *cfg, int64_t T, const void *x, 
                                const moe_weights *w, void *h, void *y_pairs, void *hs, void *z,
                                float *ab, float *abs, void *stream);
 
-/* The two halves of moe_expert_ffn, for callers that schedule or time them
+/* The two halves of moe_expert_ffn (the SwiGLU FFN's gate/up projection with the
+ * activation, then its down projection), for callers that schedule or time them
  * separately (same arguments and outputs as above):
  *   moe_expert_up:   h (and hs when hs != NULL) from x
  *   moe_expert_down: y_pairs from h (and z from hs when both are non-NULL) */
@@ -236,8 +239,11 @@ moe_status moe_combine(const moe_config *cfg, int64_t T, const void *u, const vo
                        const void *y_pairs, const moe_routing *r, const float *topk_w,
                        void *out, void *stream);
 
-/* Whole layer: moe_gate -> moe_permute -> moe_expert_ffn -> moe_combine on one
- * stream, every intermediate in `ws` (>= moe_workspace_size bytes, 256-byte aligned).
+/* Whole layer (notes page, "DeepSeekMoE" total-output equation
+ * h'_t = u_t + FFN_share(u_t) + sum_r g_{r,t} FFN_r(u_t), computed as the MoE
+ * forward's steps: gate, per-expert FFNs on the chosen tokens, weighted sum):
+ * moe_gate -> moe_permute -> moe_expert_ffn -> moe_combine on one stream, every
+ * intermediate in `ws` (>= moe_workspace_size bytes, 256-byte aligned).
  *   x [T, D] act dtype;  out [T, D] act dtype (must not alias x)
  *   topk_idx [T, K] int32 / topk_w [T, K] fp32: optional copies of the routing (NULL = skip) */
 moe_status moe_forward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
