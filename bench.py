@@ -520,9 +520,10 @@ def library_probe(reps: int = 8) -> None:
 
     Times moe_expert_up on that routing (routed experts only), torch.bmm on the same
     products with the weights stored k-major, and one dense 65536 x 4096 x 7168 product
-    (the same flops against a single weight matrix).  Random bf16 operands; medians of
-    `reps` calls after two warm-up calls.  Run it under rocprofv3 --pmc to read the clock
-    and MFMA occupancy of each launch."""
+    (the same flops against a single weight matrix); then moe_expert_up alone with every
+    expert holding 64 .. 512 rows.  Random bf16 operands; medians of `reps` calls after two
+    warm-up calls.  Run it under rocprofv3 --pmc to read the clock and MFMA occupancy of
+    each launch."""
     import torch
     from routed_expert_moe_amd import binding as B, configs
     sh = configs.V3_PREFILL_BF16
@@ -566,6 +567,31 @@ def library_probe(reps: int = 8) -> None:
         st = stats(ts)
         out[name] = {"ms": st, "tflops_median": flops / (st["median"] / 1e3) / 1e12}
         progress(f"library probe {name}: {st['median']:.3f} ms")
+    # the routed launch alone as the rows per expert vary (every expert the same count)
+    del a, bk, c, a2, b2, c2
+    sweep = {}
+    for rows in (64, 128, 192, 256, 384, 512):
+        Tr = rows * E // K
+        xr = torch.randn(Tr, D, device=dev, dtype=torch.bfloat16, generator=g)
+        tr = torch.arange(Tr, device=dev, dtype=torch.int32)[:, None] * K + torch.arange(K, device=dev, dtype=torch.int32)
+        rr = B.make_routing(cfg, Tr)
+        B.moe_permute(cfg, Tr, (tr % E).to(torch.int32).contiguous(), rr)
+        hr = torch.empty(rr.struct.max_rows, I, device=dev, dtype=torch.bfloat16)
+        ts = []
+        for i in range(reps + 2):
+            ev[0].record()
+            B.moe_expert_up(cfg, Tr, xr, rr, wts, hr)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(ev[0].elapsed_time(ev[1]))
+        med = stats(ts)["median"]
+        fl = 2.0 * Tr * K * D * 2 * I
+        sweep[str(rows)] = {"T": Tr, "ms_median": med, "tflops": fl / (med / 1e3) / 1e12,
+                            "w13_read_once_tbs": E * 2 * I * D * 2 / (med / 1e3) / 1e12}
+        progress(f"library probe rows per expert {rows}: {med:.3f} ms")
+        del xr, rr, hr
+    out["moe_expert_up_rows_per_expert"] = sweep
     print(json.dumps({"library_probe": out}), flush=True)
 
 
