@@ -240,16 +240,18 @@ hipError_t launch_gate_route(const moe_config &cfg, int64_t T, const float *logi
 
 // ---------------------------------------------------------------------------
 // Gate logits for small batches (T < 64, bf16): l[t][e] = x_t . W_g[e].
-// A GEMM tile would leave most CUs idle here.  Each workgroup takes 4 expert
-// rows; its 8 wavefronts split K eight ways and form the dot products of up to
-// 8 tokens per pass in fp32 (lanes stride over their K range in 16-byte
-// pieces), sum the 16 lanes of each row with DPP moves, then add the rows and
-// wavefronts in LDS in a fixed order.
+// A GEMM tile would leave most CUs idle here.  Each workgroup takes one expert
+// row (E workgroups: at E = 256 every CU streams one row of W_g; four rows per
+// workgroup kept 64 CUs busy and took 1.8 us longer per V3 decode step); its 8
+// wavefronts split K eight ways and form the dot products of up to 8 tokens per
+// pass in fp32 (lanes stride over their K range in 16-byte pieces), sum the 16
+// lanes of each row with DPP moves, then add the rows and wavefronts in LDS in a
+// fixed order.
 namespace moe {
 namespace {
 
 constexpr int kGemvTokens = 8;
-constexpr int kGemvExperts = 4;
+constexpr int kGemvExperts = 1;
 constexpr int kGemvWaves = 8;
 
 __device__ __forceinline__ void bf16x8_to_f32(const u32x4_t v, float (&f)[8]) {
