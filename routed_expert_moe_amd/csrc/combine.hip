@@ -67,28 +67,35 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int D, int
         }
       }
     };
+    // every load of the first batch (u, z and kBatch y rows) goes out before the first sum;
+    // the sums keep their order: u, z, then slots 0..K-1
     u32x4_t vu[CH], vz[CH];
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       vu[q] = residual ? load(u, t, q) : load(y, 0, q);
       vz[q] = z != nullptr ? load(z, t, q) : load(y, 0, q);
     }
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      if (residual) add_row(q, vu[q], 1.0f, false);
-      if (z != nullptr) add_row(q, vz[q], 1.0f, false);
-    }
     for (int k0 = 0; k0 < K; k0 += kBatch) {
+      int row[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) row[i] = s_row[min(k0 + i, K - 1)];
       u32x4_t v[CH][kBatch];
 #pragma unroll
       for (int q = 0; q < CH; ++q)
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) v[q][i] = load(y, max(s_row[min(k0 + i, K - 1)], 0), q);
+        for (int i = 0; i < kBatch; ++i) v[q][i] = load(y, max(row[i], 0), q);
+      if (k0 == 0) {
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+          if (residual) add_row(q, vu[q], 1.0f, false);
+          if (z != nullptr) add_row(q, vz[q], 1.0f, false);
+        }
+      }
 #pragma unroll
       for (int q = 0; q < CH; ++q)
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-          if (k0 + i < K && s_row[k0 + i] >= 0) add_row(q, v[q][i], s_w[k0 + i], true);
+          if (k0 + i < K && row[i] >= 0) add_row(q, v[q][i], s_w[k0 + i], true);
     }
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
