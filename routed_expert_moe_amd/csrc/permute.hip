@@ -68,18 +68,26 @@ __device__ void write_units(const PermArgs &a, int e, int off, int cnt, int padd
   }
 }
 
-// inclusive Hillis-Steele scan of v[0, kMaxE) in LDS, two entries per thread (kPermThreads)
+// inclusive scan of v[0, kMaxE) in LDS: every thread takes two consecutive entries, each
+// wavefront scans its 64 pair sums by shuffles, and the wavefront totals are added in
+// wavefront order (two barriers; integer sums, so the result is exact)
 __device__ void scan_lds(int *v) {
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    int v0 = 0, v1 = 0;
-    const int i0 = threadIdx.x, i1 = threadIdx.x + kPermThreads;
-    if (i0 >= off) v0 = v[i0 - off];
-    if (i1 >= off) v1 = v[i1 - off];
-    __syncthreads();
-    v[i0] += v0;
-    v[i1] += v1;
-    __syncthreads();
+  static_assert(kMaxE == 2 * kPermThreads, "two entries per thread");
+  __shared__ int s_wave[kPermWaves];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int lo = v[2 * t], hi = v[2 * t + 1];
+  int x = lo + hi;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
   }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) x += s_wave[w];
+  v[2 * t] = x - hi;
+  v[2 * t + 1] = x;
+  __syncthreads();
 }
 
 // the chunk table from counts and padded ends (TM == 128); s_u is LDS scratch of kMaxE
@@ -158,10 +166,11 @@ __device__ void count_block(const PermArgs &a, int blk, int (*s_cnt)[kMaxE]) {
 // phase 2, one workgroup of kPermThreads
 __device__ void scan_all(const PermArgs &a, int *s_pad, int *s_cnt_e, int *s_u) {
   for (int e = threadIdx.x; e < a.E; e += kPermThreads) {
-    // exclusive prefix over the count workgroups, eight histogram entries loaded at a time
-    // (one dependent load per entry left a global round trip per workgroup)
+    // exclusive prefix over the count workgroups, 32 histogram entries loaded at a time
+    // (one dependent load per entry left a global round trip per workgroup; the V3
+    // prefill batch has 32 count workgroups, so one round trip)
     int run = 0;
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 32;
     for (int b0 = 0; b0 < a.nblk; b0 += kBatch) {
       int v[kBatch];
 #pragma unroll
