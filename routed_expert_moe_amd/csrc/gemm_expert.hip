@@ -43,8 +43,10 @@
 // contiguous ranges, one per XCD (workgroup b runs on XCD b % 8).
 //
 // Epilogue: SwiGLU (silu(gate) * up in fp32) or plain; the bf16 tile is staged
-// in LDS and written as whole row runs.  Only rows that hold a real pair
-// (routed) or a token (dense) are written; padding rows keep unspecified values.
+// in LDS and written as whole row runs with the non-temporal hint (h and y_pairs are
+// read back only after the whole launch, long evicted; 1-2% faster per launch at V3).
+// Only rows that hold a real pair (routed) or a token (dense) are written; padding
+// rows keep unspecified values.
 // A training forward can also keep the SwiGLU's inputs: with c_save set, each
 // real row's gate and up pre-activations are stored in fp32 straight from the
 // accumulators (16 bytes per lane), so the backward need not recompute them.
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_expert_kernel(ExpertWork wk)
         const int gcol = col0 + cc * 8;
         if (gcol >= ncols) continue;
         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ot + lr * LDR + cc * 16);
-        *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(c_base) + static_cast<int64_t>(row0 + lr) * ldc + gcol) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(c_base) + static_cast<int64_t>(row0 + lr) * ldc + gcol));
       }
       __syncthreads();   // the next item's loads refill this LDS
       // gfx9 counts stores in vmcnt: drain them so the next item's waits count only its loads
