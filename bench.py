@@ -52,8 +52,8 @@ PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector)
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     "prefill_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-                   "sha256": "e82bd00bd8bd5b049c85eb060cfa49809888942fe324a4c4dd5e9678cc105e47",
-                   "fetch_kib": 12199832, "write_kib": 294912,
+                   "sha256": "cc5405a0485a7dcae974229ecbc26d0f06bd2e2c0f937aa80f8b871c8fd37b0e",
+                   "fetch_kib": 12114830, "write_kib": 294927,
                    "profile": "profiles/gemm_expert_gate_up_v3_prefill_T8192_counters.md"},
     "decode_up": {"sources": ("gemm_skinny.hip", "common.hpp"),
                   "sha256": "8a86871ecd0fe49301b9a4f87bb3f4bf23a9523c288db51e2882de059ffe939c",
@@ -64,12 +64,12 @@ COUNTERS = {
                 "fetch_kib": 5046430, "write_kib": 190350,
                 "profile": "profiles/gemm_fp8_gate_up_v3_prefill_w8a8_T8192_counters.md"},
     "v2_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-              "sha256": "e82bd00bd8bd5b049c85eb060cfa49809888942fe324a4c4dd5e9678cc105e47",
-              "fetch_kib": 3110751, "write_kib": 98304,
+              "sha256": "cc5405a0485a7dcae974229ecbc26d0f06bd2e2c0f937aa80f8b871c8fd37b0e",
+              "fetch_kib": 3114970, "write_kib": 98512,
               "profile": "profiles/gemm_expert_gate_up_v2_T4096_counters.md"},
     "ep_up": {"sources": ("gemm_expert.hip", "common.hpp"),
-              "sha256": "e82bd00bd8bd5b049c85eb060cfa49809888942fe324a4c4dd5e9678cc105e47",
-              "fetch_kib": 1283557, "write_kib": 32768,
+              "sha256": "cc5405a0485a7dcae974229ecbc26d0f06bd2e2c0f937aa80f8b871c8fd37b0e",
+              "fetch_kib": 1294826, "write_kib": 32769,
               "profile": "profiles/gemm_expert_gate_up_v3_ep_shard_T4096_E32_counters.md"},
 }
 
